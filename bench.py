@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Throughput of the S3D8 weight-decode-fused linear layer on one MI355X.
+
+Headline workload: the decode-step GEMV of the Llama-3.2-11B text MLP
+gate/up shape, M=1 token, K=4096, N=14336 (Y = X W^T), S3D8 weights packed
+by the library's packer from N(0, 0.02) fp32 weights, activations N(0,1)
+quantised per token on the GPU.  One step = s3d8_quant_act + s3d8_linear on
+one token, inputs resident in HBM.  The metric is effective weight GB/s:
+the S3D8 bytes of the matrix (packed bytes + bf16 channel scales + the
+96-byte table) per step time.
+
+To keep the weights out of the 256 MB Infinity Cache the step cycles
+through R distinct device copies of the packed matrix (the pages' own
+practice of cycling source tensors), R * 19.6 MB >= 2 x 256 MB.  The steps
+are captured once in a HIP graph (R steps, one per copy) and replayed, so
+host launch overhead does not enter the timed region.
+
+Also reported: the prefill GEMM (M=2048, K=4096, N=14336) in INT8 TOPS
+against the INT8 MFMA peak, the dominant kernel's roofline fraction, and the
+CPU oracle timed on the host cores (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POPS
+MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
+METRIC = "effective weight GB/s (% HBM peak) at M=1; INT8 TOPS (% MFMA peak) at M=2048"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "w2_a8_matmul_amd", "csrc", "s3d8_kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name, launches_bytes):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, only if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def per_kernel_us(torch, fn, n, spin_cycles=50_000_000):
+    """Average GPU duration of fn() (one kernel launch) from events around
+    each launch.  A spin kernel queued first holds the stream until every
+    launch and event is queued, so host gaps do not enter the intervals."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return float(d.mean()), float(np.median(d))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=560)
+    ap.add_argument("--warmup", type=int, default=56)
+    ap.add_argument("--pack-iters", type=int, default=25)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build runs the S3D8 linear on a single MI355X "
+              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import w2_a8_matmul_amd as s3d8
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    # ---------------------------------------------------------------- decode GEMV workload
+    lin = workloads.C1[1]
+    M, K, N = lin.M, lin.K, lin.N
+    T = s3d8.num_triples(N)
+    weight_bytes = s3d8.format_bytes(N, K)                   # 19,603,554
+    kernel_bytes = weight_bytes + M * K + 4 * M + 4 * M * N  # + xq, xs, y
+    log(f"workload {lin.name}: M={M} K={K} N={N}, {weight_bytes} S3D8 bytes")
+    t0 = time.time()
+    W = workloads.weights(lin)
+    C, scales, packed = s3d8.pack(W, seed=lin.pack_seed, max_iters=args.pack_iters)
+    del W
+    log(f"packed in {time.time() - t0:.1f}s")
+    R = int(np.ceil(2 * MALL_BYTES / weight_bytes))
+    R = max(R, 2)
+    dC = torch.from_numpy(C).to(dev)
+    dS = torch.from_numpy(scales.view(np.int16)).to(dev)
+    dP = [torch.from_numpy(packed).to(dev) for _ in range(R)]
+    xs_host = workloads.activations(lin)
+    dX = [torch.from_numpy(xs_host).to(dev) for _ in range(R)]
+    xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+    xsc = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def step(r):
+        s3d8.quant_act(dX[r], xq, xsc)
+        s3d8.linear(xq, xsc, dP[r], dC, dS, N, y=y)
+
+    # eager warm-up, then capture R steps in one graph
+    for i in range(3):
+        step(i % R)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(R):
+            step(r)
+    rem = args.steps % R
+    graph_rem = None
+    if rem:
+        graph_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph_rem):
+            for r in range(rem):
+                step(r)
+    torch.cuda.synchronize()
+
+    for i in range(0, args.warmup, R):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps (graph of {R} steps, R={R} weight copies)")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps // R):
+        graph.replay()
+    if graph_rem is not None:
+        graph_rem.replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / args.steps
+    value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # dominant kernel: s3d8_linear (the GEMV), its own duration
+    xq_w, xs_w = s3d8.quant_act(dX[0])
+    lin_mean_us, lin_med_us = per_kernel_us(
+        torch, lambda i: s3d8.linear(xq_w, xs_w, dP[i % R], dC, dS, N, y=y), 4 * R)
+    qa_mean_us, _ = per_kernel_us(torch, lambda i: s3d8.quant_act(dX[i % R], xq, xsc), 2 * R)
+    achieved = kernel_bytes / (lin_mean_us * 1e-6) / 1e9
+    traffic = measured_traffic("gemv_c1_m1", kernel_bytes)
+    log(f"step {ms_per_step * 1e3:.2f} us -> {value:.1f} GB/s; linear kernel {lin_mean_us:.2f} us "
+        f"(median {lin_med_us:.2f}) -> {achieved:.1f} GB/s; quant_act {qa_mean_us:.2f} us")
+    del dP, dX
+
+    # ---------------------------------------------------------------- prefill GEMM
+    prefill = None
+    if not args.no_prefill:
+        lp = workloads.C3
+        t0 = time.time()
+        Wp = workloads.weights(lp)
+        Cp, Sp, Pp = s3d8.pack(Wp, seed=lp.pack_seed, max_iters=args.pack_iters)
+        del Wp
+        log(f"prefill weights packed in {time.time() - t0:.1f}s")
+        xp = torch.from_numpy(workloads.activations(lp)).to(dev)
+        xqp, xsp = s3d8.quant_act(xp)
+        Rp = 4
+        dPp = [torch.from_numpy(Pp).to(dev) for _ in range(Rp)]
+        dCp = torch.from_numpy(Cp).to(dev)
+        dSp = torch.from_numpy(Sp.view(np.int16)).to(dev)
+        yp = torch.empty((lp.M, lp.N), dtype=torch.float32, device=dev)
+        for i in range(2):
+            s3d8.linear(xqp, xsp, dPp[i % Rp], dCp, dSp, lp.N, y=yp)
+        torch.cuda.synchronize()
+        nrep = 20
+        g_mean_us, g_med_us = per_kernel_us(
+            torch, lambda i: s3d8.linear(xqp, xsp, dPp[i % Rp], dCp, dSp, lp.N, y=yp), nrep)
+        ops = 2.0 * lp.M * lp.K * lp.N
+        tops = ops / (g_mean_us * 1e-6) / 1e12
+        log(f"prefill GEMM {lp.name}: {g_mean_us:.1f} us -> {tops:.1f} TOPS")
+        prefill = {
+            "workload": f"{lp.name}: M={lp.M} K={lp.K} N={lp.N}",
+            "value": round(tops, 2), "unit": "INT8 TOPS", "us_per_launch": round(g_mean_us, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
+                         "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                         "traffic": measured_traffic("gemm_c3", None)},
+        }
+        del dPp
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        import json as _json
+
+        with open(os.path.join(ROOT, "tests", "golden", "centroids.json")) as f:
+            Cg = np.array(_json.load(f)[f"cfg{lin.config_id}.mat{lin.matrix_id}"]["C"], np.uint8)
+        W = workloads.weights(lin)
+        alpha_o, packed_o = oracle.encode(W, Cg)
+        del W
+        x = workloads.activations(lin)
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            oracle.linear(x, packed_o, Cg, alpha_o, N)
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        el = time.perf_counter() - t0
+        cpu = {"value": round(weight_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"full {lin.name} step (quantise, decode every weight, naive int dot "
+                         f"products, fp32 epilogue) repeated {n} times in {el:.1f} s"}
+        log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": f"{lin.name}: decode GEMV M={M} K={K} N={N} (Llama-3.2-11B text MLP "
+                               f"gate/up), S3D8 weights packed from N(0,0.02), step = quant_act + linear",
+                   "weight_copies": R, "graph_steps": R},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "s3d8_linear (gemv)", "kernel_us": round(lin_mean_us, 3),
+                     "algorithmic_bytes": kernel_bytes},
+        "quant_act_us": round(qa_mean_us, 3),
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * s3d8.h -- C ABI of libs3d8: the S3D8 weight-decode-fused linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page and section):
+ *   [BLOG]  "11 billion parameters on a phone" (Graphcore Research blog):
+ *           "S3D8: a 2.7-bit weight format for fast decoding", "Bit layout",
+ *           "Output channel packing", "Fused matrix-vector product",
+ *           "Fast? How fast?".
+ *   [PAPER] "Llama-Mobile: Efficient 2.7-Bit Quantization of VLMs" (arXiv),
+ *           Sec. 3.4 "The S3D8 Format" (Eq. 1 and the "Quantization"
+ *           equations), Sec. 4 and Sec. 4.3, Appendix A.3.
+ *
+ * Format (canonical layout, used by every entry point):
+ *   A weight matrix W has N output channels and K input columns (Y = X W^T,
+ *   [PAPER] Sec. 4.3).  Channels are grouped in triples t = 0 .. T-1 with
+ *   T = ceil(N/3); the channel count is padded to Npad = 3T ([PAPER] Sec. 3.4
+ *   after Eq. 1).  Three buffers describe the matrix:
+ *     centroids   uint8 [32][3], row-major: the absolute-value centroid table
+ *                 C, integers in [0,127] ([BLOG] "S3D8"; [PAPER] Eq. 1).
+ *     scales      uint16 [Npad]: bfloat16 bit patterns of the channel scales
+ *                 alpha_i = max_j |W_ij| / 127 ([PAPER] "Quantization");
+ *                 padded channels hold 0.
+ *     packed      uint8 [T][K], row-major, K-contiguous per triple: byte
+ *                 (t, j) holds channels 3t, 3t+1, 3t+2 at input column j
+ *                 ([BLOG] "Output channel packing").  Its bits, from bit 7 to
+ *                 bit 0, are [S2 xor S0, S1, Q4..Q0, S0] ([BLOG] "Bit
+ *                 layout"): Q is the shared centroid index, S_d = 1 selects
+ *                 the negative value for channel 3t+d.
+ *   Decoded weight ([PAPER] Eq. 1):  W~_ij = alpha_i * s_ij * C[q][i mod 3]
+ *   where q is the index of byte (floor(i/3), j) and s_ij = -1 if S_{i mod 3}
+ *   is set, else +1.  The channel-INT8 weight w_ij = s_ij * C[q][i mod 3]
+ *   lies in [-127, 127].
+ *
+ * Activations: per-token ("channel-scaled") INT8 ([PAPER] Sec. 4, A.3).  For
+ *   row m of X: s_m = max_j |x_mj| / 127 (IEEE fp32 division), and
+ *   xq_mj = clamp(round_half_even(x_mj / s_m), -127, 127); an all-zero row has
+ *   s_m = 0 and xq = 0.
+ *
+ * Linear ([BLOG] "Fused matrix-vector product"):
+ *   acc_mn = sum_j xq_mj * w_nj (exact INT32),
+ *   y_mn   = (s_m * float(acc_mn)) * float(alpha_n)   (fp32, left to right).
+ *
+ * Conventions for every entry point:
+ *   - Status codes: S3D8_OK (0) on success, a positive S3D8_ERR_* otherwise.
+ *     s3d8_last_error() returns a message for the calling thread's most
+ *     recent failure.  No C++ exception crosses the ABI.
+ *   - All arguments are validated on the host before any GPU work is
+ *     queued; a failed validation queues nothing.
+ *   - Sizes are int64_t element counts.  K must be a positive multiple of 16
+ *     (the blog's fused loop also steps 16 columns); M, N positive.
+ *   - The caller allocates and owns every buffer.  The library keeps no
+ *     pointer after a call returns.
+ *   - Device entry points take device pointers (e.g. torch tensors'
+ *     data_ptr()) and a hipStream_t passed as `void *` (NULL = the default
+ *     stream).  They only enqueue work and return; results are ready when
+ *     the stream is synchronised.  A fault inside a kernel surfaces at that
+ *     synchronisation, not in the return code.
+ *   - Pointers marked "16-B aligned" must be multiples of 16 bytes.
+ */
+#ifndef S3D8_H
+#define S3D8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define S3D8_OK 0
+#define S3D8_ERR_INVALID_ARG 1 /* null pointer, non-positive size, bad option   */
+#define S3D8_ERR_SHAPE 2       /* K not a multiple of 16, or a size too large   */
+#define S3D8_ERR_ALIGN 3       /* a pointer that must be 16-B aligned is not    */
+#define S3D8_ERR_HIP 4         /* the HIP runtime reported an error             */
+#define S3D8_ERR_NOMEM 5       /* host allocation failed                        */
+#define S3D8_ERR_DEVICE 6      /* the current device is not a gfx950 GPU        */
+
+/* ABI version of this header (major * 10000 + minor * 100 + patch). */
+int32_t s3d8_version(void);
+
+/* T = ceil(N/3), the number of channel triples ([PAPER] Eq. 1: q has
+ * ceil(n/3) rows).  Returns -1 if N <= 0. */
+int64_t s3d8_num_triples(int64_t N);
+
+/* Bytes of the packed index/sign matrix: ceil(N/3) * K.  -1 on bad sizes. */
+int64_t s3d8_packed_bytes(int64_t N, int64_t K);
+
+/* Total storage of one matrix: packed bytes + 2 * 3*ceil(N/3) scale bytes +
+ * 96 table bytes, i.e. about (8/3 + 16/K) bits per weight ([PAPER] Sec. 3.4).
+ * -1 on bad sizes. */
+int64_t s3d8_format_bytes(int64_t N, int64_t K);
+
+/* Message describing the calling thread's most recent failed call (empty
+ * string if none).  The pointer stays valid until the thread's next call. */
+const char *s3d8_last_error(void);
+
+/* ------------------------------------------------------------------ host */
+
+/* Fit the centroid table and encode a matrix ([PAPER] Sec. 3.4
+ * "Quantization"): alpha = bf16(max|W_i|/127), W' = |W|/alpha grouped into
+ * 3-vectors (padded channels 0), k-means++ seeding then Lloyd-Max
+ * iterations on all vectors, C = round-half-even(centres) clamped to
+ * [0,127], then the frozen-centroid encode of s3d8_encode.
+ *   W            host fp32 [N][K], row-major, finite values.
+ *   seed         seed of the k-means++ draws (SplitMix64, counter form).
+ *   max_iters    Lloyd iteration limit (>= 0); the fit also stops when no
+ *                assignment changes.
+ *   num_threads  host threads (0 = all hardware threads).  The result does
+ *                not depend on it.
+ *   centroids    out, host uint8 [32][3].
+ *   scales_bf16  out, host uint16 [3*ceil(N/3)].
+ *   packed       out, host uint8 [ceil(N/3)][K].
+ *   distortion   optional out (NULL to skip), host double [max_iters + 1]:
+ *                sum of squared distances of the vectors to their nearest
+ *                centre after seeding (index 0) and after each iteration.
+ *   iterations   optional out (NULL to skip): Lloyd iterations run.
+ * Synchronous; touches no GPU.  Errors: INVALID_ARG, SHAPE, NOMEM. */
+int32_t s3d8_pack(const float *W, int64_t N, int64_t K, uint64_t seed, int32_t max_iters,
+                  int32_t num_threads, uint8_t *centroids, uint16_t *scales_bf16,
+                  uint8_t *packed, double *distortion, int32_t *iterations);
+
+/* Frozen-centroid quantiser ([PAPER] Sec. 3.4, QAT phase; also the
+ * "direct cast" of the blog's QAT section): alpha as in s3d8_pack,
+ * s_ij = +1 if W_ij >= 0 else -1 (so -0.0 is positive), q = the index of
+ * the nearest centroid row to the scaled-absolute 3-vector in fp64, lowest
+ * index on ties; bytes per the [BLOG] bit layout; padded channels have
+ * alpha 0, value 0 and sign selector 0.
+ *   W            host fp32 [N][K].
+ *   centroids    host uint8 [32][3], every entry in [0,127].
+ *   scales_bf16  out, host uint16 [3*ceil(N/3)].
+ *   packed       out, host uint8 [ceil(N/3)][K].
+ * Synchronous; touches no GPU.  Errors: INVALID_ARG, SHAPE. */
+int32_t s3d8_encode(const float *W, int64_t N, int64_t K, const uint8_t *centroids,
+                    int32_t num_threads, uint16_t *scales_bf16, uint8_t *packed);
+
+/* ---------------------------------------------------------------- device */
+
+/* Per-token INT8 activation quantisation (see "Activations" above).
+ *   x    device fp32 [M][K], 16-B aligned, finite.
+ *   xq   out, device int8 [M][K], 16-B aligned.
+ *   xs   out, device fp32 [M].
+ * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
+int32_t s3d8_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, void *stream);
+
+/* The fused linear layer: decode S3D8 weights on the fly, INT8 x INT8
+ * products accumulated exactly in INT32, fp32 epilogue (see "Linear").
+ *   xq           device int8 [M][K], 16-B aligned (from s3d8_quant_act).
+ *   xs           device fp32 [M].
+ *   packed       device uint8 [ceil(N/3)][K], 16-B aligned.
+ *   centroids    device uint8 [32][3].
+ *   scales_bf16  device uint16 [3*ceil(N/3)] (entries >= N are not read).
+ *   y            out, device fp32 [M][N], row-major.
+ *   acc_out      optional out (NULL to skip), device int32 [M][N]: the
+ *                accumulators before the epilogue, for verification.
+ * M <= 16 runs the decode GEMV kernel (one pass over the weights); larger M
+ * runs the MFMA GEMM kernel.  Both read the same canonical layout.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
+int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *packed, const uint8_t *centroids, const uint16_t *scales_bf16,
+                    float *y, int32_t *acc_out, void *stream);
+
+/* Decode a whole matrix to channel-INT8 ([PAPER] Eq. 1 without alpha; the
+ * blog's standalone S3D8 -> INT8 dequantisation).
+ *   packed     device uint8 [ceil(N/3)][K], 16-B aligned.
+ *   centroids  device uint8 [32][3].
+ *   w          out, device int8 [N][K], 16-B aligned; padded channels are
+ *              not written.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
+int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K,
+                     int8_t *w, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* S3D8_H */

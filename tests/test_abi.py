@@ -1,0 +1,135 @@
+"""The C ABI on the host (no GPU): the library loads, exports every symbol
+declared in include/s3d8.h with the expected behaviour of its size helpers,
+and every device entry point rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import w2_a8_matmul_amd as s3d8
+from w2_a8_matmul_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "s3d8.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(s3d8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    syms = _declared_symbols()
+    for name in ["s3d8_pack", "s3d8_encode", "s3d8_quant_act", "s3d8_linear", "s3d8_dequant",
+                 "s3d8_last_error", "s3d8_num_triples", "s3d8_packed_bytes", "s3d8_format_bytes",
+                 "s3d8_version"]:
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+        assert name in _lib.SIGNATURES, name
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (s3d8_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(_declared_symbols()) <= exported
+
+
+def test_size_helpers():
+    L = _lib.lib()
+    assert L.s3d8_version() >= 10000
+    assert L.s3d8_num_triples(14336) == 4779
+    assert L.s3d8_num_triples(384) == 128
+    assert L.s3d8_num_triples(0) == -1
+    assert L.s3d8_packed_bytes(14336, 4096) == 4779 * 4096
+    assert L.s3d8_format_bytes(14336, 4096) == 19_603_554
+    assert L.s3d8_format_bytes(128256, 4096) == 175_368_800
+    assert L.s3d8_packed_bytes(-1, 16) == -1
+
+
+def _err(name, *args):
+    rc = getattr(_lib.lib(), name)(*args)
+    msg = _lib.lib().s3d8_last_error().decode()
+    return rc, msg
+
+
+# Fake device-looking addresses: validation must fail before any dereference
+# or HIP call, so these are never touched.
+A16 = 0x10000
+A_ODD = 0x10001
+
+
+def test_quant_act_validation():
+    assert _err("s3d8_quant_act", None, 1, 16, A16, A16, None)[0] == _lib.S3D8_ERR_INVALID_ARG
+    assert _err("s3d8_quant_act", A16, 0, 16, A16, A16, None)[0] == _lib.S3D8_ERR_INVALID_ARG
+    rc, msg = _err("s3d8_quant_act", A16, 1, 24, A16, A16, None)
+    assert rc == _lib.S3D8_ERR_SHAPE and "16" in msg
+    assert _err("s3d8_quant_act", A_ODD, 1, 16, A16, A16, None)[0] == _lib.S3D8_ERR_ALIGN
+
+
+def test_linear_validation():
+    good = dict(xq=A16, xs=A16, M=1, K=64, N=9, packed=A16, C=A16, s=A16, y=A16, acc=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return _err("s3d8_linear", a["xq"], a["xs"], a["M"], a["K"], a["N"], a["packed"], a["C"],
+                    a["s"], a["y"], a["acc"], None)[0]
+
+    assert call(xq=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(y=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(C=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(M=0) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(N=-3) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(K=40) == _lib.S3D8_ERR_SHAPE
+    assert call(packed=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(xq=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(M=1 << 31) == _lib.S3D8_ERR_SHAPE
+    assert call(N=1 << 30, K=1 << 12) == _lib.S3D8_ERR_SHAPE
+
+
+def test_dequant_validation():
+    L = _lib.lib()
+    assert L.s3d8_dequant(None, A16, 3, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_dequant(A16, A16, 3, 8, A16, None) == _lib.S3D8_ERR_SHAPE
+    assert L.s3d8_dequant(A16, A16, 3, 16, A_ODD, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_dequant(A16, A16, 0, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+
+
+def test_host_validation_errors():
+    W = np.zeros((3, 16), np.float32)
+    with pytest.raises(s3d8.S3D8Error) as e:
+        s3d8.pack(np.zeros((3, 8), np.float32))
+    assert e.value.code == _lib.S3D8_ERR_SHAPE
+    with pytest.raises(s3d8.S3D8Error) as e:
+        s3d8.pack(W, max_iters=-1)
+    assert e.value.code == _lib.S3D8_ERR_INVALID_ARG
+    bad = np.full((32, 3), 128, np.uint8)
+    with pytest.raises(s3d8.S3D8Error) as e:
+        s3d8.encode(W, bad)
+    assert e.value.code == _lib.S3D8_ERR_INVALID_ARG and "127" in str(e.value)
+    L = _lib.lib()
+    assert L.s3d8_pack(None, 3, 16, 0, 1, 1, A16, A16, A16, None, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_encode(W.ctypes.data, 3, 16, None, 1, A16, A16) == _lib.S3D8_ERR_INVALID_ARG
+
+
+def test_last_error_cleared_by_success():
+    W = np.zeros((3, 16), np.float32)
+    with pytest.raises(s3d8.S3D8Error):
+        s3d8.pack(np.zeros((3, 8), np.float32))
+    assert _lib.lib().s3d8_last_error().decode() != ""
+    s3d8.encode(W, np.ones((32, 3), np.uint8))
+    assert _lib.lib().s3d8_last_error().decode() == ""
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(ImportError):
+        _lib.lib()

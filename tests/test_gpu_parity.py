@@ -1,0 +1,231 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: INT8 codes, activation scales, decoded weights and INT32 accumulators
+bit-exact; fp32 outputs within 1e-6 relative error of the oracle (and zero
+where the oracle's output is zero).  The epilogue is two fp32 multiplies in a
+fixed order, so the outputs are also expected to be bit-identical; that is
+checked too.
+
+Small shapes are compared element by element over whole outputs; full-size
+workloads are compared in full where the oracle finishes in seconds, and on
+sampled outputs (each computed by the oracle one by one) otherwise.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity_inputs import packed_matrix, random_format
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+s3d8 = pytest.importorskip("w2_a8_matmul_amd")
+
+REL = 1e-6
+
+
+def dev(a, device):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def check_y(y_gpu, y_ref):
+    y_gpu = np.asarray(y_gpu, np.float32)
+    y_ref = np.asarray(y_ref, np.float32)
+    err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
+    assert (err <= REL * np.abs(y_ref.astype(np.float64))).all(), float(err.max())
+    assert (y_gpu[y_ref == 0] == 0).all()
+    np.testing.assert_array_equal(y_gpu, y_ref)
+
+
+def run_linear(x, C, alpha, packed, N, device):
+    xd = dev(x, device)
+    xq, xs = s3d8.quant_act(xd)
+    y, acc = s3d8.linear(xq, xs, dev(packed, device), dev(C, device),
+                         dev(alpha.view(np.int16), device), N, return_acc=True)
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), xs.cpu().numpy(), acc.cpu().numpy(), y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ quant_act
+def _edge_rows(K):
+    x = np.zeros((6, K), np.float32)
+    x[0, K // 3] = -2.5
+    x[1, :] = 0.7
+    x[2, :8] = [127.0, 2.5, 3.5, -2.5, -3.5, 0.5, 1.5, -0.5]
+    tiny = np.float32(2.0 ** -149)
+    x[4, :3] = [tiny * np.float32(100), tiny * np.float32(3), -tiny * np.float32(50)]
+    x[5, :] = workloads.gaussian_matrix([2000, K], 1, K)[0] * np.float32(1e-39)  # subnormal row
+    return x
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (1, 256), (3, 48), (8, 4096), (1, 14336), (37, 1280),
+                                 (1601, 5120), (2048, 4096)])
+def test_quant_act_matches_oracle(gpu, M, K):
+    x = workloads.gaussian_matrix([2001, M, K], M, K)
+    if M >= 6:
+        x[:6] = _edge_rows(K)
+    xq, xs = s3d8.quant_act(dev(x, gpu))
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(xs.cpu().numpy(), xs_ref)
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_ref)
+
+
+def test_quant_act_outlier_activations(gpu):
+    lin = workloads.C2[6]
+    x = workloads.activations(lin, M=4)
+    xq, xs = s3d8.quant_act(dev(x, gpu))
+    xq_ref, xs_ref = oracle.quant_act(x)
+    np.testing.assert_array_equal(xs.cpu().numpy(), xs_ref)
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_ref)
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("N,K", [(3, 16), (4, 16), (5, 48), (384, 256), (100, 1040), (1281, 5120)])
+def test_dequant_matches_oracle(gpu, N, K):
+    C, _, packed = random_format([2010, N, K], N, K)
+    w = s3d8.dequant(dev(packed, gpu), dev(C, gpu), N)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(w.cpu().numpy(), oracle.decode(packed, C, N, K))
+
+
+def test_dequant_every_byte_value(gpu):
+    C = workloads.uniform_centroids([2011], 0, 127)
+    packed = np.tile(np.arange(256, dtype=np.uint8), 2).reshape(2, 256)
+    w = s3d8.dequant(dev(packed, gpu), dev(C, gpu), 6)
+    np.testing.assert_array_equal(w.cpu().numpy(), oracle.decode(packed, C, 6, 256))
+
+
+def test_dequant_full_gate_up(gpu):
+    lin = workloads.C1[1]
+    C, _, packed = packed_matrix(lin)
+    w = s3d8.dequant(dev(packed, gpu), dev(C, gpu), lin.N)
+    np.testing.assert_array_equal(w.cpu().numpy(), oracle.decode(packed, C, lin.N, lin.K))
+
+
+# ------------------------------------------------------------------ linear, small
+def test_linear_random_format_config(gpu):
+    """M=1, K=256, N=384: random centroid table, uniform bytes, lognormal bf16 scales."""
+    lin = workloads.C0
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, lin.N)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(xs, xs_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+FUZZ = [(m, k, n) for m in (1, 2, 3, 5, 8, 9, 16, 17, 33) for (k, n) in
+        [(16, 1), (16, 3), (48, 4), (64, 47), (80, 50), (256, 48), (1040, 97)]]
+
+
+@pytest.mark.parametrize("M,K,N", FUZZ)
+def test_linear_shape_fuzz(gpu, M, K, N):
+    """Ragged N (mod 3 in {0,1,2}, partial triple tiles), K not a multiple of
+    the 64-column block, M spanning one and several row tiles."""
+    C, alpha, packed = random_format([2020, M, K, N], N, K)
+    x = workloads.gaussian_matrix([2021, M, K], M, K)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu)
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+def test_linear_extreme_accumulators(gpu):
+    """Largest magnitudes: every weight +-127, every activation code +-127,
+    K = 14336: |acc| = K * 127^2 fits INT32."""
+    K, N = 14336, 6
+    C = np.full((32, 3), 127, np.uint8)
+    packed = np.zeros((2, K), np.uint8)
+    packed[0, :] = 0x3E  # all positive
+    packed[1, :] = 0x7F  # all negative
+    alpha = oracle.f32_to_bf16(np.full(6, 1.0, np.float32))
+    x = np.full((2, K), 3.0, np.float32)
+    x[1] *= -1
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu)
+    big = K * 127 * 127
+    assert acc.tolist() == [[big] * 3 + [-big] * 3, [-big] * 3 + [big] * 3]
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    check_y(y, y_r)
+
+
+def test_linear_zero_rows_and_zero_scales(gpu):
+    K, N = 128, 10
+    C, alpha, packed = random_format([2030], N, K)
+    alpha[4] = 0
+    x = workloads.gaussian_matrix([2031], 3, K)
+    x[1] = 0
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu)
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+    assert (y[1] == 0).all() and (y[:, 4] == 0).all()
+
+
+# ------------------------------------------------------------------ linear, full size
+def _full_compare(lin, gpu, M=None):
+    M = lin.M if M is None else M
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin, M)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, lin.N)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+def _sampled_compare(lin, gpu, nsamples=512):
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu)
+    xq_r, xs_r = oracle.quant_act(x)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(xs, xs_r)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2040, lin.config_id, lin.matrix_id])))
+    ms = list(g.integers(0, lin.M, nsamples)) + [0, lin.M - 1, 0, lin.M - 1]
+    ns = list(g.integers(0, lin.N, nsamples)) + [0, 0, lin.N - 1, lin.N - 1]
+    ref = np.array([oracle.acc_one(xq_r[m], packed, C, lin.K, n) for m, n in zip(ms, ns)], np.int64)
+    got = acc[np.array(ms), np.array(ns)].astype(np.int64)
+    np.testing.assert_array_equal(got, ref)
+    acc_s = ref.astype(np.int32).reshape(-1, 1)
+    for i, (m, n) in enumerate(zip(ms, ns)):
+        y_r = oracle.epilogue(acc_s[i:i + 1], xs_r[m:m + 1], alpha[n:n + 1], 1)
+        check_y(y[m, n:n + 1].reshape(1, 1), y_r)
+    # the whole output is finite and padded channels never leak in
+    assert y.shape == (lin.M, lin.N) and np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_linear_gate_up_decode(gpu, m):
+    _full_compare(workloads.C1[m], gpu)
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_linear_decoder_layer(gpu, idx):
+    _full_compare(workloads.C2[idx], gpu)
+
+
+def test_linear_lm_head_decode(gpu):
+    _full_compare(workloads.C4[0], gpu)
+
+
+def test_linear_prefill_gemm_sampled(gpu):
+    _sampled_compare(workloads.C3, gpu)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_linear_prefill_c4_sampled(gpu, idx):
+    _sampled_compare(workloads.C4[idx], gpu)
+
+
+def test_linear_repeated_calls_are_identical(gpu):
+    lin = workloads.C0
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin)
+    outs = [run_linear(x, C, alpha, packed, lin.N, gpu)[2] for _ in range(3)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])

@@ -1,0 +1,173 @@
+"""S3D8 weight-decode-fused linear layer for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libs3d8.so`` (``include/s3d8.h``):
+argument marshalling only.  Host functions take numpy arrays; device
+functions take torch tensors (device memory and the current HIP stream) and
+run the library's HIP kernels.  There is no fallback path: if the library
+is missing, importing ``w2_a8_matmul_amd._lib`` raises.
+
+Format: the S3D8 storage format of "Llama-Mobile: Efficient 2.7-Bit
+Quantization of VLMs" (Sec. 3.4, Eq. 1) with the byte layout of the blog
+"11 billion parameters on a phone" ("Bit layout").
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import S3D8Error, call, lib  # noqa: F401
+
+__all__ = [
+    "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "pack", "encode",
+    "quant_act", "linear", "dequant", "PackedLinear",
+]
+
+
+def _np_ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_triples(N: int) -> int:
+    return int(lib().s3d8_num_triples(N))
+
+
+def packed_bytes(N: int, K: int) -> int:
+    return int(lib().s3d8_packed_bytes(N, K))
+
+
+def format_bytes(N: int, K: int) -> int:
+    return int(lib().s3d8_format_bytes(N, K))
+
+
+# ------------------------------------------------------------------ host
+def pack(W, seed: int = 1, max_iters: int = 50, num_threads: int = 0, return_stats: bool = False):
+    """Fit centroids (k-means++ / Lloyd-Max) and encode W (fp32 [N][K]).
+
+    Returns (centroids uint8 [32][3], scales_bf16 uint16 [3T], packed uint8
+    [T][K]) and, with ``return_stats``, also (distortion per iteration,
+    iterations)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    T = num_triples(N)
+    C = np.empty((32, 3), np.uint8)
+    scales = np.empty((3 * T,), np.uint16)
+    packed = np.empty((T, K), np.uint8)
+    dist = np.zeros((max(max_iters, 0) + 1,), np.float64)
+    iters = ctypes.c_int32(0)
+    call("s3d8_pack", _np_ptr(W), N, K, seed, max_iters, num_threads, _np_ptr(C), _np_ptr(scales),
+         _np_ptr(packed), _np_ptr(dist), ctypes.byref(iters))
+    if return_stats:
+        return C, scales, packed, dist[: iters.value + 1].copy(), iters.value
+    return C, scales, packed
+
+
+def encode(W, centroids, num_threads: int = 0):
+    """Frozen-centroid encode: returns (scales_bf16 [3T], packed [T][K])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    C = np.ascontiguousarray(centroids, dtype=np.uint8)
+    N, K = W.shape
+    T = num_triples(N)
+    scales = np.empty((3 * T,), np.uint16)
+    packed = np.empty((T, K), np.uint8)
+    call("s3d8_encode", _np_ptr(W), N, K, _np_ptr(C), num_threads, _np_ptr(scales), _np_ptr(packed))
+    return scales, packed
+
+
+# ------------------------------------------------------------------ device
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev_check(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def quant_act(x, xq=None, xs=None):
+    """Per-token INT8 quantisation of fp32 x [M][K] on the GPU: (xq, xs)."""
+    torch = _torch()
+    _dev_check(x, torch.float32, "x")
+    M, K = x.shape
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        call("s3d8_quant_act", x.data_ptr(), M, K, xq.data_ptr(), xs.data_ptr(), _stream(x))
+    return xq, xs
+
+
+def linear(xq, xs, packed, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False):
+    """Fused S3D8 linear: y fp32 [M][N] (and the INT32 accumulators)."""
+    torch = _torch()
+    _dev_check(xq, torch.int8, "xq")
+    _dev_check(xs, torch.float32, "xs")
+    _dev_check(packed, torch.uint8, "packed")
+    _dev_check(centroids, torch.uint8, "centroids")
+    if scales.dtype == torch.bfloat16:
+        scales = scales.view(torch.int16)
+    _dev_check(scales, scales.dtype, "scales")
+    M, K = xq.shape
+    T = num_triples(N)
+    if packed.numel() != T * K or centroids.numel() != 96 or scales.numel() < 3 * T:
+        raise ValueError("packed / centroids / scales do not match (N, K)")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if return_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    with torch.cuda.device(xq.device):
+        call("s3d8_linear", xq.data_ptr(), xs.data_ptr(), M, K, N, packed.data_ptr(),
+             centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
+             acc.data_ptr() if acc is not None else None, _stream(xq))
+    if return_acc:
+        return y, acc
+    return y
+
+
+def dequant(packed, centroids, N: int, w=None):
+    """Standalone decode to channel-INT8: w int8 [N][K]."""
+    torch = _torch()
+    _dev_check(packed, torch.uint8, "packed")
+    _dev_check(centroids, torch.uint8, "centroids")
+    T, K = packed.shape
+    if T != num_triples(N):
+        raise ValueError("packed rows do not match N")
+    if w is None:
+        w = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    with torch.cuda.device(packed.device):
+        call("s3d8_dequant", packed.data_ptr(), centroids.data_ptr(), N, K, w.data_ptr(), _stream(packed))
+    return w
+
+
+class PackedLinear:
+    """An S3D8 weight matrix resident in device memory."""
+
+    def __init__(self, centroids, scales, packed, N: int, device="cuda"):
+        torch = _torch()
+        self.N = int(N)
+        self.K = int(packed.shape[1])
+        self.centroids = torch.as_tensor(np.ascontiguousarray(centroids, np.uint8)).to(device)
+        self.scales = torch.as_tensor(np.ascontiguousarray(scales, np.uint16).view(np.int16)).to(device)
+        self.packed = torch.as_tensor(np.ascontiguousarray(packed, np.uint8)).to(device)
+
+    @classmethod
+    def from_weights(cls, W, seed: int = 1, max_iters: int = 50, device="cuda"):
+        C, s, p = pack(W, seed=seed, max_iters=max_iters)
+        return cls(C, s, p, W.shape[0], device)
+
+    def __call__(self, x):
+        xq, xs = quant_act(x)
+        return linear(xq, xs, self.packed, self.centroids, self.scales, self.N)

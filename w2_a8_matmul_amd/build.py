@@ -1,0 +1,59 @@
+"""Build libs3d8.so in-tree: HIP kernels for gfx950 with hipcc, the host
+packer with g++, linked by hipcc.  Needs no GPU (hipcc cross-compiles)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libs3d8.so")
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    # exact arithmetic: no contraction into FMA, IEEE division, no FTZ
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
+    # no packed fp32 instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-march=x86-64-v3", "-ffp-contract=off",
+              "-fno-fast-math", "-pthread", "-I", INCLUDE, "-I", CSRC]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and (re)link libs3d8.so; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for name in sorted(os.listdir(CSRC)):
+        src = os.path.join(CSRC, name)
+        base, ext = os.path.splitext(name)
+        obj = os.path.join(BUILD, base + ".o")
+        if ext == ".hip":
+            _run([HIPCC, *HIP_FLAGS, "-c", src, "-o", obj], verbose)
+        elif ext == ".cpp":
+            _run(["g++", *HOST_FLAGS, "-c", src, "-o", obj], verbose)
+        else:
+            continue
+        objs.append(obj)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs, "-pthread"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -78,7 +78,9 @@ C4 = [
 def weights(lin: Linear) -> np.ndarray:
     """fp32 [N][K] ~ N(0, 0.02)."""
     g = rng(lin.config_id, T_WEIGHT, lin.matrix_id)
-    return (g.standard_normal((lin.N, lin.K), dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+    W = g.standard_normal((lin.N, lin.K), dtype=np.float32)
+    W *= np.float32(0.02)
+    return W
 
 
 def activations(lin: Linear, M: int | None = None) -> np.ndarray:
