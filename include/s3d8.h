@@ -142,27 +142,61 @@ int32_t s3d8_encode(const float *W, int64_t N, int64_t K, const uint8_t *centroi
  * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
 int32_t s3d8_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, void *stream);
 
-/* The fused linear layer: decode S3D8 weights on the fly, INT8 x INT8
- * products accumulated exactly in INT32, fp32 epilogue (see "Linear").
+/* Bytes of the tiled device layout of a matrix (see s3d8_tile):
+ * ceil(ceil(N/3)/16) * ceil(K/64) * 1024.  -1 on bad sizes. */
+int64_t s3d8_tiled_bytes(int64_t N, int64_t K);
+
+/* Re-lay a packed matrix into the tiled device layout read by s3d8_linear
+ * and s3d8_forward.  The bytes are unchanged ([BLOG] "Bit layout"); only
+ * their order in memory changes, once, before the weights are used (as the
+ * blog permutes its lookup tables once before model load).  The matrix is cut
+ * into fragments of 16 channel triples x 64 input columns; fragment
+ * (tile i, column block b) occupies 1 KiB at byte offset (i*ceil(K/64) + b)
+ * * 1024, and inside it the 16 bytes at offset 16*L (L = n + 16*g, n < 16,
+ * g < 4) are packed[16i + n][64b + 16g .. 64b + 16g + 15], zero past the last
+ * triple or past K.  This is the operand layout of the gfx950 instruction
+ * v_mfma_i32_16x16x64_i8 for 16 triples, so each wave reads a fragment as one
+ * contiguous 1 KiB load.
+ *   packed  device uint8 [ceil(N/3)][K] (canonical layout).
+ *   tiled   out, device uint8 [s3d8_tiled_bytes(N, K)], 16-B aligned.
+ * Errors: INVALID_ARG, SHAPE (more than 2^31 tiled bytes), ALIGN, DEVICE, HIP. */
+int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, void *stream);
+
+/* The fused linear layer on pre-quantised activations: decode S3D8 weights
+ * on the fly, INT8 x INT8 products accumulated exactly in INT32, fp32
+ * epilogue (see "Linear").
  *   xq           device int8 [M][K], 16-B aligned (from s3d8_quant_act).
  *   xs           device fp32 [M].
- *   packed       device uint8 [ceil(N/3)][K], 16-B aligned.
- *   centroids    device uint8 [32][3].
+ *   tiled        device, the matrix in the tiled layout of s3d8_tile,
+ *                16-B aligned.
+ *   centroids    device uint8 [32][3], 4-B aligned.
  *   scales_bf16  device uint16 [3*ceil(N/3)] (entries >= N are not read).
  *   y            out, device fp32 [M][N], row-major.
  *   acc_out      optional out (NULL to skip), device int32 [M][N]: the
  *                accumulators before the epilogue, for verification.
- * M <= 16 runs the decode GEMV kernel (one pass over the weights); larger M
- * runs the MFMA GEMM kernel.  Both read the same canonical layout.
  * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
 int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                    const uint8_t *packed, const uint8_t *centroids, const uint16_t *scales_bf16,
+                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
                     float *y, int32_t *acc_out, void *stream);
+
+/* The whole path from fp32 activations: per-token INT8 quantisation (as
+ * s3d8_quant_act) followed by the fused linear (as s3d8_linear).  For M <= 4
+ * (and M * ceil(ceil(K/64)/16) <= 16) both run in one kernel launch; otherwise
+ * s3d8_quant_act and s3d8_linear are enqueued in turn.  Results are
+ * identical to calling the two entry points.
+ *   x            device fp32 [M][K], 16-B aligned, finite.
+ *   tiled, centroids, scales_bf16, y, acc_out   as for s3d8_linear.
+ *   xq           out, device int8 [M][K], 16-B aligned: the activation codes.
+ *   xs           out, device fp32 [M]: the activation scales.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
+int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                     const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq,
+                     float *xs, int32_t *acc_out, void *stream);
 
 /* Decode a whole matrix to channel-INT8 ([PAPER] Eq. 1 without alpha; the
  * blog's standalone S3D8 -> INT8 dequantisation).
  *   packed     device uint8 [ceil(N/3)][K], 16-B aligned.
- *   centroids  device uint8 [32][3].
+ *   centroids  device uint8 [32][3], 4-B aligned.
  *   w          out, device int8 [N][K], 16-B aligned; padded channels are
  *              not written.
  * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */

@@ -90,8 +90,34 @@ def test_linear_validation():
     assert call(K=40) == _lib.S3D8_ERR_SHAPE
     assert call(packed=A_ODD) == _lib.S3D8_ERR_ALIGN
     assert call(xq=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(C=A16 + 2) == _lib.S3D8_ERR_ALIGN
     assert call(M=1 << 31) == _lib.S3D8_ERR_SHAPE
     assert call(N=1 << 30, K=1 << 12) == _lib.S3D8_ERR_SHAPE
+
+
+def test_tile_and_forward_validation():
+    L = _lib.lib()
+    assert L.s3d8_tiled_bytes(14336, 4096) == 299 * 64 * 1024
+    assert L.s3d8_tiled_bytes(3, 16) == 1024
+    assert L.s3d8_tiled_bytes(0, 16) == -1
+    assert L.s3d8_tile(None, 3, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_tile(A16, 3, 24, A16, None) == _lib.S3D8_ERR_SHAPE
+    assert L.s3d8_tile(A16, 3, 16, A_ODD, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_tile(A16, 1 << 31, 4096, A16, None) == _lib.S3D8_ERR_SHAPE
+
+    def fwd(**kw):
+        a = dict(x=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, xq=A16, xs=A16, acc=None)
+        a.update(kw)
+        return L.s3d8_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["C"], a["s"], a["y"], a["xq"],
+                              a["xs"], a["acc"], None)
+
+    assert fwd(x=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(xq=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(xs=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(K=8) == _lib.S3D8_ERR_SHAPE
+    assert fwd(x=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert fwd(t=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert fwd(C=A16 + 1) == _lib.S3D8_ERR_ALIGN
 
 
 def test_dequant_validation():
@@ -99,6 +125,7 @@ def test_dequant_validation():
     assert L.s3d8_dequant(None, A16, 3, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
     assert L.s3d8_dequant(A16, A16, 3, 8, A16, None) == _lib.S3D8_ERR_SHAPE
     assert L.s3d8_dequant(A16, A16, 3, 16, A_ODD, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_dequant(A16, A16 + 1, 3, 16, A16, None) == _lib.S3D8_ERR_ALIGN
     assert L.s3d8_dequant(A16, A16, 0, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
 
 

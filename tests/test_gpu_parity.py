@@ -39,13 +39,43 @@ def check_y(y_gpu, y_ref):
     np.testing.assert_array_equal(y_gpu, y_ref)
 
 
+def relayout(packed, K):
+    """The tiled device layout, from its definition in include/s3d8.h:
+    fragment (tile i, block b) at (i*KB + b)*1024, lane L = n + 16g owns the
+    16 bytes packed[16i+n][64b+16g ..], zero past the matrix."""
+    T = packed.shape[0]
+    tiles, KB = (T + 15) // 16, (K + 63) // 64
+    P = np.zeros((tiles * 16, KB * 64), np.uint8)
+    P[:T, :K] = packed
+    return P.reshape(tiles, 16, KB, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+
+
 def run_linear(x, C, alpha, packed, N, device):
     xd = dev(x, device)
     xq, xs = s3d8.quant_act(xd)
-    y, acc = s3d8.linear(xq, xs, dev(packed, device), dev(C, device),
-                         dev(alpha.view(np.int16), device), N, return_acc=True)
+    tiled = s3d8.tile(dev(packed, device), N)
+    y, acc = s3d8.linear(xq, xs, tiled, dev(C, device), dev(alpha.view(np.int16), device), N,
+                         return_acc=True)
     torch.cuda.synchronize()
     return xq.cpu().numpy(), xs.cpu().numpy(), acc.cpu().numpy(), y.cpu().numpy()
+
+
+def run_forward(x, C, alpha, packed, N, device):
+    tiled = s3d8.tile(dev(packed, device), N)
+    y, xq, xs, acc = s3d8.forward(dev(x, device), tiled, dev(C, device),
+                                  dev(alpha.view(np.int16), device), N, return_all=True)
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), xs.cpu().numpy(), acc.cpu().numpy(), y.cpu().numpy()
+
+
+# ------------------------------------------------------------------ tiled layout
+@pytest.mark.parametrize("N,K", [(3, 16), (48, 64), (50, 80), (385, 1040), (14336, 4096)])
+def test_tile_matches_relayout(gpu, N, K):
+    _, _, packed = random_format([1990, N, K], N, K)
+    tiled = s3d8.tile(dev(packed, gpu), N)
+    torch.cuda.synchronize()
+    assert tiled.numel() == s3d8.tiled_bytes(N, K)
+    np.testing.assert_array_equal(tiled.cpu().numpy(), relayout(packed, K))
 
 
 # ------------------------------------------------------------------ quant_act
@@ -229,3 +259,49 @@ def test_linear_repeated_calls_are_identical(gpu):
     outs = [run_linear(x, C, alpha, packed, lin.N, gpu)[2] for _ in range(3)]
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
+
+
+# ------------------------------------------------------------------ forward (quantise + linear)
+FWD = [(m, k, n) for m in (1, 2, 3, 4, 5, 16) for (k, n) in [(16, 3), (80, 50), (1040, 97), (4096, 300),
+                                                            (14336, 64), (16384, 48)]]
+
+
+@pytest.mark.parametrize("M,K,N", FWD)
+def test_forward_matches_oracle(gpu, M, K, N):
+    """s3d8_forward: one fused launch for small M (quantisation inside the
+    GEMV), quant_act + linear otherwise; both must equal the oracle."""
+    C, alpha, packed = random_format([2050, M, K, N], N, K)
+    x = workloads.gaussian_matrix([2051, M, K], M, K)
+    if M >= 2:
+        x[1] = 0.0  # an all-zero token
+    xq, xs, acc, y = run_forward(x, C, alpha, packed, N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(xs, xs_r)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+@pytest.mark.parametrize("idx", range(7))
+def test_forward_decoder_layer(gpu, idx):
+    """The decode step of one decoder layer through s3d8_forward."""
+    lin = workloads.C2[idx]
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin)
+    xq, xs, acc, y = run_forward(x, C, alpha, packed, lin.N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, lin.N)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(xs, xs_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+def test_forward_gate_up_m1(gpu):
+    lin = workloads.C1[1]
+    C, alpha, packed = packed_matrix(lin)
+    x = workloads.activations(lin)
+    xq, xs, acc, y = run_forward(x, C, alpha, packed, lin.N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, lin.N)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)

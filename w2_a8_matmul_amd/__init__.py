@@ -19,8 +19,8 @@ import numpy as np
 from ._lib import S3D8Error, call, lib  # noqa: F401
 
 __all__ = [
-    "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "pack", "encode",
-    "quant_act", "linear", "dequant", "PackedLinear",
+    "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "tiled_bytes", "pack", "encode",
+    "tile", "quant_act", "linear", "forward", "dequant", "PackedLinear",
 ]
 
 
@@ -39,6 +39,10 @@ def packed_bytes(N: int, K: int) -> int:
 
 def format_bytes(N: int, K: int) -> int:
     return int(lib().s3d8_format_bytes(N, K))
+
+
+def tiled_bytes(N: int, K: int) -> int:
+    return int(lib().s3d8_tiled_bytes(N, K))
 
 
 # ------------------------------------------------------------------ host
@@ -110,30 +114,84 @@ def quant_act(x, xq=None, xs=None):
     return xq, xs
 
 
-def linear(xq, xs, packed, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False):
-    """Fused S3D8 linear: y fp32 [M][N] (and the INT32 accumulators)."""
+def tile(packed, N: int, tiled=None):
+    """Re-lay a device packed matrix [T][K] into the tiled layout read by
+    linear/forward (done once per matrix)."""
+    torch = _torch()
+    _dev_check(packed, torch.uint8, "packed")
+    T, K = packed.shape
+    if T != num_triples(N):
+        raise ValueError("packed rows do not match N")
+    if tiled is None:
+        tiled = torch.empty((tiled_bytes(N, K),), dtype=torch.uint8, device=packed.device)
+    with torch.cuda.device(packed.device):
+        call("s3d8_tile", packed.data_ptr(), N, K, tiled.data_ptr(), _stream(packed))
+    return tiled
+
+
+def _scales_view(scales):
+    torch = _torch()
+    if scales.dtype in (torch.bfloat16, torch.uint16):
+        scales = scales.view(torch.int16)
+    _dev_check(scales, torch.int16, "scales")
+    return scales
+
+
+def _check_weights(tiled, centroids, scales, N, K):
+    torch = _torch()
+    _dev_check(tiled, torch.uint8, "tiled")
+    _dev_check(centroids, torch.uint8, "centroids")
+    T = num_triples(N)
+    if tiled.numel() < tiled_bytes(N, K) or centroids.numel() != 96 or scales.numel() < 3 * T:
+        raise ValueError("tiled / centroids / scales do not match (N, K)")
+
+
+def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False):
+    """Fused S3D8 linear on pre-quantised activations: y fp32 [M][N] (and
+    the INT32 accumulators)."""
     torch = _torch()
     _dev_check(xq, torch.int8, "xq")
     _dev_check(xs, torch.float32, "xs")
-    _dev_check(packed, torch.uint8, "packed")
-    _dev_check(centroids, torch.uint8, "centroids")
-    if scales.dtype == torch.bfloat16:
-        scales = scales.view(torch.int16)
-    _dev_check(scales, scales.dtype, "scales")
+    scales = _scales_view(scales)
     M, K = xq.shape
-    T = num_triples(N)
-    if packed.numel() != T * K or centroids.numel() != 96 or scales.numel() < 3 * T:
-        raise ValueError("packed / centroids / scales do not match (N, K)")
+    _check_weights(tiled, centroids, scales, N, K)
     if y is None:
         y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
     if return_acc and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     with torch.cuda.device(xq.device):
-        call("s3d8_linear", xq.data_ptr(), xs.data_ptr(), M, K, N, packed.data_ptr(),
+        call("s3d8_linear", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(),
              centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
              acc.data_ptr() if acc is not None else None, _stream(xq))
     if return_acc:
         return y, acc
+    return y
+
+
+def forward(x, tiled, centroids, scales, N: int, y=None, xq=None, xs=None, acc=None,
+            return_all: bool = False):
+    """The whole path from fp32 x [M][K]: quantise and apply the S3D8 linear
+    (one kernel launch for M <= 4).  Returns y, or (y, xq, xs, acc) with
+    ``return_all``."""
+    torch = _torch()
+    _dev_check(x, torch.float32, "x")
+    scales = _scales_view(scales)
+    M, K = x.shape
+    _check_weights(tiled, centroids, scales, N, K)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    if return_all and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    with torch.cuda.device(x.device):
+        call("s3d8_forward", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(),
+             scales.data_ptr(), y.data_ptr(), xq.data_ptr(), xs.data_ptr(),
+             acc.data_ptr() if acc is not None else None, _stream(x))
+    if return_all:
+        return y, xq, xs, acc
     return y
 
 
@@ -153,7 +211,7 @@ def dequant(packed, centroids, N: int, w=None):
 
 
 class PackedLinear:
-    """An S3D8 weight matrix resident in device memory."""
+    """An S3D8 weight matrix resident in device memory, in the tiled layout."""
 
     def __init__(self, centroids, scales, packed, N: int, device="cuda"):
         torch = _torch()
@@ -161,7 +219,8 @@ class PackedLinear:
         self.K = int(packed.shape[1])
         self.centroids = torch.as_tensor(np.ascontiguousarray(centroids, np.uint8)).to(device)
         self.scales = torch.as_tensor(np.ascontiguousarray(scales, np.uint16).view(np.int16)).to(device)
-        self.packed = torch.as_tensor(np.ascontiguousarray(packed, np.uint8)).to(device)
+        packed_dev = torch.as_tensor(np.ascontiguousarray(packed, np.uint8)).to(device)
+        self.tiled = tile(packed_dev, self.N)
 
     @classmethod
     def from_weights(cls, W, seed: int = 1, max_iters: int = 50, device="cuda"):
@@ -169,5 +228,4 @@ class PackedLinear:
         return cls(C, s, p, W.shape[0], device)
 
     def __call__(self, x):
-        xq, xs = quant_act(x)
-        return linear(xq, xs, self.packed, self.centroids, self.scales, self.N)
+        return forward(x, self.tiled, self.centroids, self.scales, self.N)

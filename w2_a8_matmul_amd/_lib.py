@@ -33,7 +33,10 @@ SIGNATURES = {
     "s3d8_pack": (_I32, [_P, _I64, _I64, _U64, _I32, _I32, _P, _P, _P, _P, _P]),
     "s3d8_encode": (_I32, [_P, _I64, _I64, _P, _I32, _P, _P]),
     "s3d8_quant_act": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "s3d8_tiled_bytes": (_I64, [_I64, _I64]),
+    "s3d8_tile": (_I32, [_P, _I64, _I64, _P, _P]),
     "s3d8_linear": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "s3d8_forward": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "s3d8_dequant": (_I32, [_P, _P, _I64, _I64, _P, _P]),
 }
 

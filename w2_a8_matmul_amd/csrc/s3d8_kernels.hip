@@ -49,16 +49,6 @@ __device__ __forceinline__ uint32_t signed_triple(uint32_t b, const uint8_t *C) 
     return (uint32_t)(w0 & 0xFF) | ((uint32_t)(w1 & 0xFF) << 8) | ((uint32_t)(w2 & 0xFF) << 16);
 }
 
-// Build the lane-interleaved signed table.  Every wave writes one entry to
-// 64 consecutive dwords per step.  Ends with a barrier.
-__device__ __forceinline__ void build_table(uint32_t *tab, uint8_t *cl, const uint8_t *C) {
-    const int tid = threadIdx.x, nth = blockDim.x;
-    if (tid < 96) cl[tid] = C[tid];
-    __syncthreads();
-    for (int idx = tid; idx < kTabWords; idx += nth) tab[idx] = signed_triple((uint32_t)idx >> 6, cl);
-    __syncthreads();
-}
-
 // Decode 16 packed bytes (k = 0..15 of one channel triple) into three
 // 16-byte INT8 vectors, one per channel of the triple: o_d byte k = w_d(k).
 __device__ __forceinline__ void decode16(const uint4 p, const uint32_t lane_off, const uint32_t *tab,
@@ -89,6 +79,41 @@ __device__ __forceinline__ void decode16(const uint4 p, const uint32_t lane_off,
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Raw buffer loads (buffer_load_dwordx4): an offset at or past the buffer
+// size returns zeros without touching memory, so predicated-off lanes need no
+// branch around the load.  kOOB is past every buffer (sizes are < 2^31).
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int32_t kRsrcWord3 = 0x00020000;  // gfx9 family: raw, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Stage the 96-byte centroid table (read through the scalar cache, so it does
+// not queue behind the vector loads already in flight) into LDS, then build
+// the lane-interleaved signed table.  C32 must be 4-byte aligned.  Contains
+// barriers.
+__device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *clw, const uint32_t *__restrict__ C32) {
+    uint32_t cw[24];
+#pragma unroll
+    for (int i = 0; i < 24; ++i) cw[i] = C32[i];
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    }
+    __syncthreads();
+    const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
+    for (int idx = threadIdx.x; idx < kTabWords / 4; idx += blockDim.x) {
+        const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+        reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+    }
+    __syncthreads();
+}
 
 // --------------------------------------------------------------- quant_act
 
@@ -134,102 +159,336 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *_
     }
 }
 
+// --------------------------------------------------------------- tiled layout
+
+// The device weight layout that the linear kernels read.  The canonical
+// matrix (triple rows of K bytes) is cut into fragments of 16 triples x 64
+// columns; fragment (tile i, block b) is stored as 1 KiB at byte offset
+// (i * KB + b) * 1024 with KB = ceil(K/64), and inside it lane L = n + 16g of
+// a wave owns bytes [16L, 16L+16) = packed[16i + n][64b + 16g .. +15] (zero
+// past the last triple or past K).  That is the B-operand layout of
+// v_mfma_i32_16x16x64_i8 for 16 triples, so a wave reads each fragment as
+// one fully contiguous 1 KiB load.  Like the blog's table permutation, the
+// re-layout is done once before the weights are used.
+constexpr int kTileThreads = 256;
+
+__global__ __launch_bounds__(kTileThreads) void tile_kernel(const uint8_t *__restrict__ packed, int K, int T,
+                                                            int KB, int64_t nchunks,
+                                                            uint8_t *__restrict__ tiled) {
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(packed, (uint32_t)T * (uint32_t)K);
+    for (int64_t c = (int64_t)blockIdx.x * kTileThreads + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * kTileThreads) {
+        const int64_t frag = c >> 6;
+        const int l = (int)(c & 63);
+        const int64_t tile = frag / KB;
+        const int blk = (int)(frag - tile * KB);
+        const int64_t t = tile * 16 + (l & 15);
+        const int k = blk * 64 + (l >> 4) * 16;
+        const uint32_t off = (t < T && k < K) ? (uint32_t)t * (uint32_t)K + (uint32_t)k : kOOB;
+        *reinterpret_cast<uint4 *>(tiled + c * 16) = bload16(rp, off);
+    }
+}
+
 // --------------------------------------------------------------- GEMV
 
-// Decode GEMV for up to 16 token rows (and, tiled over blockIdx.y, any M).
+// Decode GEMV for up to 16 token rows.
 //
-// Workgroup = kGemvWaves waves sharing one tile of 16 channel triples (48
-// output channels) and splitting K between them.  Each wave runs
-// v_mfma_i32_16x16x64_i8: the A operand holds the 16 token rows of X, the B
-// operand the decoded weights of the 16 triples for one channel d of the
-// triple, so three MFMAs (d = 0, 1, 2) consume one 64-column block of the
-// packed matrix.  Lane L = n + 16*g holds A row n / B column n and bytes
-// [16g, 16g + 16) of the 64-column block: its packed bytes are one 16-byte
-// load of triple row n, and after decode16 they are already in B layout.
-// Partial sums of the waves are added in LDS; the epilogue multiplies by
-// the token scale and the bf16 channel scale and writes fp32.
-constexpr int kGemvWaves = 8;
-constexpr int kGemvThreads = kGemvWaves * 64;
-constexpr int kGemvUnroll = 4;
+// Work item = one tile of 16 channel triples (48 output channels).  A
+// workgroup of WAVES waves builds the decode table once, then loops over
+// tiles (persistent when there are more tiles than resident workgroups).
+// Its waves split K: wave w owns 64-column blocks [w*kbw, (w+1)*kbw).  Each
+// wave runs v_mfma_i32_16x16x64_i8 with the (up to) 16 token rows of X as
+// the A operand and the decoded weights of the 16 triples for channel d of
+// the triple as the B operand: three MFMAs (d = 0, 1, 2) per 64-column
+// block.  Lane L = n + 16*g holds A row n / B column n and bytes
+// [16g, 16g+16) of the block; its weight bytes are one contiguous 16-byte
+// slice of the fragment, already in B layout after decode16.
+//
+// Each wave walks its (tile, chunk of U blocks) steps with two register
+// buffers: the loads of the next step (possibly the next tile's first chunk)
+// are in flight while the current one is decoded.  Every wave has the same
+// number of steps per tile (blocks past its range are predicated off), so
+// the per-tile barriers line up.  Wave partial sums meet in LDS through
+// integer atomics (exact, order-free); the epilogue multiplies by the token
+// scale and the bf16 channel scale and writes fp32.
+//
+// FUSED (M <= 4): the kernel also quantises the fp32 activations.  Each wave
+// loads its own K range of x first (before any weight load, since vector
+// loads retire in order), the workgroup reduces the row absmax through LDS,
+// and each wave writes its INT8 codes to a private LDS slice from which the
+// A operands are read.  Workgroup 0 also stores xq and xs for the caller.
+template <int U>
+struct GemvBuf {
+    uint4 p[U];
+    v4i x[U];
+};
 
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
-    const int8_t *__restrict__ xq, const float *__restrict__ xs, int M, int K, int N, int T,
-    const uint8_t *__restrict__ packed, const uint8_t *__restrict__ centroids,
+constexpr int kFusedMaxRows = 4;
+constexpr int kFusedXF4 = 4;  // at most this many float4 of x per lane in the fused prologue
+
+template <int WAVES, int U, bool FUSED>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
+    const int8_t *__restrict__ xq, const float *__restrict__ xs, const float *__restrict__ xf,
+    int8_t *__restrict__ xq_out, float *__restrict__ xs_out, int M, int K, int N, int T,
+    const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids,
     const uint16_t *__restrict__ scales, float *__restrict__ y, int32_t *__restrict__ acc_out,
-    int kb_per_wave) {
+    int kbw) {
+    constexpr int kThreads = WAVES * 64;
     __shared__ uint32_t tab[kTabWords];
-    __shared__ uint8_t cl[96];
+    __shared__ int32_t red[16 * 48];
+    __shared__ uint32_t clw[24];
+    __shared__ float rmax[FUSED ? WAVES * kFusedMaxRows : 1];
+    __shared__ float srow[FUSED ? kFusedMaxRows : 1];
+    extern __shared__ int8_t xw[];  // FUSED: [WAVES][M][64 * kbw] INT8 codes, then 16 zero bytes
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int t = blockIdx.x * 16 + n;   // triple of B column n
-    const int m = blockIdx.y * 16 + n;   // token row of A row n
     const int KB = (K + 63) >> 6;
-    const int kb0 = wave * kb_per_wave;
-    const int kb1 = min(KB, kb0 + kb_per_wave);
-    const bool tvalid = t < T, mvalid = m < M;
-    const uint8_t *prow = packed + (int64_t)(tvalid ? t : 0) * K + g * 16;
-    const int8_t *xrow = xq + (int64_t)(mvalid ? m : 0) * K + g * 16;
+    const int tiles = (T + 15) >> 4;
+    const int kb0 = min(KB, wave * kbw);
+    const int kb1 = min(KB, kb0 + kbw);
+    const int nchunks = (kbw + U - 1) / U;  // uniform across the workgroup
     const uint32_t lane_off = (uint32_t)lane << 2;
 
-    // first block of loads goes out before the table is built
-    uint4 pk[kGemvUnroll];
-    v4i xa[kGemvUnroll];
-    auto load = [&](int kb) {
+    // The small inputs on every workgroup's critical path go out first, ahead
+    // of the weight stream: the centroid table (scalar loads), this thread's
+    // epilogue scales, and (fused) the wave's slice of x.
+    uint32_t cw[24];
 #pragma unroll
-        for (int u = 0; u < kGemvUnroll; ++u) {
-            const int b = kb + u;
-            const bool ok = b < kb1 && (b * 64 + g * 16) < K;
-            pk[u] = (ok && tvalid) ? *reinterpret_cast<const uint4 *>(prow + (int64_t)b * 64)
-                                   : make_uint4(0, 0, 0, 0);
-            xa[u] = (ok && mvalid) ? *reinterpret_cast<const v4i *>(xrow + (int64_t)b * 64)
-                                   : v4i{0, 0, 0, 0};
+    for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+    // epilogue: output idx = tid + j * kThreads is (row idx / 48, channel
+    // idx % 48 of the tile); its scales are fetched a tile ahead
+    constexpr int kEp = (16 * 48 + kThreads - 1) / kThreads;
+    float ep_sx[kEp], ep_a[kEp];
+    auto ep_scale = [&](int t16, int j) {
+        const int idx = tid + j * kThreads;
+        const int ch = t16 * 48 + idx % 48;
+        return (idx < M * 48 && ch < N) ? bf16_to_f32(scales[ch]) : 0.0f;
+    };
+#pragma unroll
+    for (int j = 0; j < kEp; ++j) {
+        const int idx = tid + j * kThreads;
+        ep_sx[j] = 0.0f;
+        if constexpr (!FUSED) {
+            if (idx < M * 48) ep_sx[j] = xs[idx / 48];
+        }
+        ep_a[j] = blockIdx.x < (unsigned)((T + 15) >> 4) ? ep_scale(blockIdx.x, j) : 0.0f;
+    }
+
+    // fused prologue, part 1: this wave's slice of x
+    float4 xv[kFusedXF4];
+    const int span4 = 16 * kbw;                   // float4 per row in the wave's K range
+    const int nf4 = (M * span4 + 63) >> 6;        // float4 per lane actually used (<= kFusedXF4)
+    if constexpr (FUSED) {
+        const __amdgpu_buffer_rsrc_t rf = make_rsrc(xf, (uint32_t)M * (uint32_t)K * 4u);
+#pragma unroll
+        for (int i = 0; i < kFusedXF4; ++i) {
+            if (i < nf4) {
+                const int f = lane + 64 * i;
+                const int m = f / span4, r = f - m * span4;
+                const int k = kb0 * 64 + 4 * r;
+                const bool ok = m < M && k < K;
+                xv[i] = __builtin_bit_cast(
+                    float4, bload16(rf, ok ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 4u : kOOB));
+            }
+        }
+    }
+
+    for (int i = tid; i < 16 * 48; i += kThreads) red[i] = 0;
+    if constexpr (FUSED) {
+        if (tid < 4) reinterpret_cast<uint32_t *>(xw + WAVES * M * 64 * kbw)[tid] = 0u;  // zero block
+    }
+
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xq, FUSED ? 0u : (uint32_t)M * (uint32_t)K);
+    const uint32_t xbase = (!FUSED && n < M) ? (uint32_t)n * (uint32_t)K + g * 16 : kOOB;
+    auto load = [&](GemvBuf<U> &b, int tile, int c) {
+        const uint32_t fbase = ((uint32_t)tile * (uint32_t)KB + (uint32_t)(kb0 + c * U)) * 1024u + (uint32_t)lane * 16u;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int blk = kb0 + c * U + u;  // wave-uniform
+            if (blk < kb1) {
+                b.p[u] = bload16(rt, fbase + u * 1024u);
+                if constexpr (!FUSED)
+                    b.x[u] = __builtin_bit_cast(
+                        v4i, bload16(rx, (blk * 64 + g * 16 < K) ? xbase + (uint32_t)blk * 64 : kOOB));
+            }
         }
     };
-    if (kb0 < kb1) load(kb0);
 
-    build_table(tab, cl, centroids);
+    // fused prologue, part 2: per-row absmax of the wave's slice.  This waits
+    // for x before the first weight load is issued: behind the weight stream
+    // of all CUs, x would arrive much later, and every wave of the workgroup
+    // needs it before the decode can start.
+    float lm[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (FUSED) {
+#pragma unroll
+        for (int i = 0; i < kFusedXF4; ++i) {
+            if (i < nf4) {
+                const int m = (lane + 64 * i) / span4;
+                const float a = fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w)));
+#pragma unroll
+                for (int r = 0; r < kFusedMaxRows; ++r) lm[r] = (m == r) ? fmaxf(lm[r], a) : lm[r];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < kFusedMaxRows; ++r) {
+            if (r < M) {
+#pragma unroll
+                for (int off = 32; off > 0; off >>= 1) lm[r] = fmaxf(lm[r], __shfl_xor(lm[r], off, 64));
+            }
+        }
+    }
+
+    GemvBuf<U> A, B;
+    int tile = blockIdx.x;
+    if (tile < tiles) load(A, tile, 0);
+
+    // signed table from the centroid words loaded at the top
+    if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    }
+    __syncthreads();
+    {
+        const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
+        for (int idx = tid; idx < kTabWords / 4; idx += kThreads) {
+            const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+            reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+        }
+    }
+    if constexpr (FUSED) {
+        if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < kFusedMaxRows; ++r)
+                if (r < M) rmax[wave * kFusedMaxRows + r] = lm[r];
+        }
+    }
+    __syncthreads();
+    if constexpr (FUSED) {
+        // fused prologue, part 3: scales, INT8 codes into this wave's LDS slice
+        float srow_r[kFusedMaxRows];
+#pragma unroll
+        for (int r = 0; r < kFusedMaxRows; ++r) {
+            float a = 0.0f;
+            if (r < M)
+                for (int w = 0; w < WAVES; ++w) a = fmaxf(a, rmax[w * kFusedMaxRows + r]);
+            srow_r[r] = (a == 0.0f) ? 0.0f : a / 127.0f;
+        }
+        if (tid < kFusedMaxRows) srow[tid] = srow_r[tid];
+        if (blockIdx.x == 0 && tid < M && xs_out) xs_out[tid] = srow_r[tid];
+#pragma unroll
+        for (int i = 0; i < kFusedXF4; ++i) {
+            if (i < nf4) {
+                const int f = lane + 64 * i;
+                const int m = f / span4, r = f - m * span4;
+                if (m < M) {
+                    float s = srow_r[0];
+#pragma unroll
+                    for (int rr = 1; rr < kFusedMaxRows; ++rr) s = (m == rr) ? srow_r[rr] : s;
+                    char4 o;
+                    if (s == 0.0f) {
+                        o = make_char4(0, 0, 0, 0);
+                    } else {
+                        o.x = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(xv[i].x / s)));
+                        o.y = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(xv[i].y / s)));
+                        o.z = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(xv[i].z / s)));
+                        o.w = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(xv[i].w / s)));
+                    }
+                    *reinterpret_cast<char4 *>(xw + ((wave * M + m) * 64 * kbw + 4 * r)) = o;
+                    const int k = kb0 * 64 + 4 * r;
+                    if (blockIdx.x == 0 && xq_out && k < K)
+                        *reinterpret_cast<char4 *>(xq_out + (int64_t)m * K + k) = o;
+                }
+            }
+        }
+    }
+
+    // fused A operand: lanes of rows < M read their codes, the others read a
+    // zero block (stride 0)
+    const int xa_base = n < M ? (wave * M + n) * 64 * kbw + g * 16 : WAVES * M * 64 * kbw;
+    const int xa_step = n < M ? 64 : 0;
 
     v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
-    for (int kb = kb0; kb < kb1; kb += kGemvUnroll) {
-        if (kb != kb0) load(kb);
+    auto process = [&](const GemvBuf<U> &b, int c) {
 #pragma unroll
-        for (int u = 0; u < kGemvUnroll; ++u) {
+        for (int u = 0; u < U; ++u) {
+            const int bl = c * U + u;
+            if (kb0 + bl >= kb1) continue;  // wave-uniform: past this wave's range
+            v4i a;
+            if constexpr (FUSED) {
+                a = *reinterpret_cast<const v4i *>(xw + (xa_base + bl * xa_step));
+            } else {
+                a = b.x[u];
+            }
             v4i b0, b1, b2;
-            decode16(pk[u], lane_off, tab, b0, b1, b2);
-            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[u], b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[u], b1, acc1, 0, 0, 0);
-            acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[u], b2, acc2, 0, 0, 0);
+            decode16(b.p[u], lane_off, tab, b0, b1, b2);
+            acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, acc1, 0, 0, 0);
+            acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b2, acc2, 0, 0, 0);
         }
-    }
+    };
 
-    // cross-wave reduction in LDS (the table is dead from here on)
-    __syncthreads();
-    int32_t *red = reinterpret_cast<int32_t *>(tab);  // [wave][d][i][lane]
+    // after the last chunk of a tile: reduce across waves, epilogue
+    auto finish = [&](int t16) {
+        // D[row r][col n] sits in lane n + 16*(r/4), element r%4; the channel
+        // of (col n, d) within the tile is 3n + d.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        red[((wave * 3 + 0) * 4 + i) * 64 + lane] = acc0[i];
-        red[((wave * 3 + 1) * 4 + i) * 64 + lane] = acc1[i];
-        red[((wave * 3 + 2) * 4 + i) * 64 + lane] = acc2[i];
-    }
-    __syncthreads();
-
-    // D[row r][col n] of the 16x16 MFMA result sits in lane n + 16*(r/4),
-    // element r%4.  Output channel of (col n, d) is 48*tile + 3n + d.
-    const int rows = min(16, M - (int)blockIdx.y * 16);
-    for (int idx = tid; idx < rows * 48; idx += kGemvThreads) {
-        const int r = idx / 48, c = idx - r * 48;
-        const int col = c / 3, d = c - col * 3;
-        const int src = (d * 4 + (r & 3)) * 64 + col + 16 * (r >> 2);
-        int32_t s = 0;
-        for (int w = 0; w < kGemvWaves; ++w) s += red[w * 3 * 4 * 64 + src];
-        const int ch = blockIdx.x * 48 + c;
-        const int row = blockIdx.y * 16 + r;
-        if (ch < N) {
-            const float v = (xs[row] * (float)s) * bf16_to_f32(scales[ch]);
-            y[(int64_t)row * N + ch] = v;
-            if (acc_out) acc_out[(int64_t)row * N + ch] = s;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            if (r < M && kb0 < kb1) {
+                atomicAdd(&red[r * 48 + 3 * n + 0], acc0[i]);
+                atomicAdd(&red[r * 48 + 3 * n + 1], acc1[i]);
+                atomicAdd(&red[r * 48 + 3 * n + 2], acc2[i]);
+            }
         }
+        acc0 = v4i{0, 0, 0, 0};
+        acc1 = v4i{0, 0, 0, 0};
+        acc2 = v4i{0, 0, 0, 0};
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kEp; ++j) {
+            const int idx = tid + j * kThreads;
+            const float a_cur = ep_a[j];
+            if (t16 + (int)gridDim.x < ((T + 15) >> 4)) ep_a[j] = ep_scale(t16 + gridDim.x, j);
+            if (idx < M * 48) {
+                const int r = idx / 48;
+                const int32_t sum = red[idx];
+                red[idx] = 0;
+                const int ch = t16 * 48 + idx % 48;
+                if (ch < N) {
+                    const float sx = FUSED ? srow[r] : ep_sx[j];
+                    const float v = (sx * (float)sum) * a_cur;
+                    y[(int64_t)r * N + ch] = v;
+                    if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    // steps (tile, c), c = 0 .. nchunks-1, alternating buffers A and B
+    int c = 0;
+    bool in_a = true;
+    while (tile < tiles) {
+        int ntile = tile, nc = c + 1;
+        if (nc == nchunks) {
+            nc = 0;
+            ntile = tile + gridDim.x;
+        }
+        const bool more = ntile < tiles;
+        if (in_a) {
+            if (more) load(B, ntile, nc);
+            process(A, c);
+        } else {
+            if (more) load(A, ntile, nc);
+            process(B, c);
+        }
+        if (nc == 0) finish(tile);
+        tile = ntile;
+        c = nc;
+        in_a = !in_a;
     }
 }
 
@@ -240,11 +499,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(
 constexpr int kDequantThreads = 512;
 
 __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
-    const uint8_t *__restrict__ packed, const uint8_t *__restrict__ centroids, int K, int N,
+    const uint8_t *__restrict__ packed, const uint32_t *__restrict__ centroids, int K, int N,
     int64_t nchunks, int8_t *__restrict__ w) {
     __shared__ uint32_t tab[kTabWords];
-    __shared__ uint8_t cl[96];
-    build_table(tab, cl, centroids);
+    __shared__ uint32_t clw[24];
+    stage_and_build_table(tab, clw, centroids);
     const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
     const int cpr = K >> 4;  // 16-byte chunks per triple row
     for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
@@ -302,6 +561,59 @@ int launch_status() {
     return S3D8_OK;
 }
 
+// Launch shapes of the GEMV: waves per workgroup, blocks per load batch, and
+// resident workgroups per CU (two 64 KiB tables fit in LDS; 16-wave groups
+// are limited to one per CU by registers).
+struct GemvConfig {
+    int waves, unroll, wgs_per_cu;
+};
+constexpr GemvConfig kGemvDefault = {16, 2, 1};
+
+struct GemvArgs {
+    const int8_t *xq;
+    const float *xs;
+    const float *xf;
+    int8_t *xq_out;
+    float *xs_out;
+    int M, K, N, T;
+    const uint8_t *tiled;
+    const uint32_t *centroids;
+    const uint16_t *scales;
+    float *y;
+    int32_t *acc_out;
+};
+
+// kbw = 64-column blocks per wave; the fused prologue needs M * kbw <= 16
+// (four float4 of x per lane).
+int gemv_kbw(int K, int waves) { return ((K + 63) / 64 + waves - 1) / waves; }
+bool gemv_fusable(int M, int K, GemvConfig cfg) { return M <= kFusedMaxRows && M * gemv_kbw(K, cfg.waves) <= 16; }
+
+// Returns false (and launches nothing) if a fused launch is asked for a shape
+// the fused prologue cannot hold.
+bool launch_gemv(GemvConfig cfg, bool fused, const GemvArgs &a, int cus, hipStream_t stream) {
+    if (a.M > 16 || (fused && !gemv_fusable(a.M, a.K, cfg))) return false;
+    const int kbw = gemv_kbw(a.K, cfg.waves);
+    const int64_t tiles = (a.T + 15) / 16;
+    const int64_t cap = (int64_t)cus * cfg.wgs_per_cu;
+    const int grid = (int)(tiles < cap ? tiles : cap);
+    const size_t xw_bytes = fused ? (size_t)cfg.waves * a.M * 64 * kbw + 16 : 0;
+#define S3D8_GEMV_CASE(W, U, F)                                                                          \
+    if (cfg.waves == W && cfg.unroll == U && fused == F) {                                               \
+        hipLaunchKernelGGL((gemv_kernel<W, U, F>), dim3(grid), dim3(W * 64), xw_bytes, stream, a.xq, a.xs, \
+                           a.xf, a.xq_out, a.xs_out, a.M, a.K, a.N, a.T, a.tiled, a.centroids, a.scales,  \
+                           a.y, a.acc_out, kbw);                                                         \
+        return true;                                                                                     \
+    }
+    S3D8_GEMV_CASE(16, 2, false)
+    S3D8_GEMV_CASE(16, 2, true)
+    S3D8_GEMV_CASE(8, 2, false)
+    S3D8_GEMV_CASE(8, 2, true)
+#undef S3D8_GEMV_CASE
+    return false;
+}
+
+int64_t tiled_bytes(int64_t N, int64_t K) { return ((N + 2) / 3 + 15) / 16 * ((K + 63) / 64) * 1024; }
+
 }  // namespace
 
 extern "C" {
@@ -319,27 +631,86 @@ int32_t s3d8_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *
     return launch_status();
 }
 
-int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                    const uint8_t *packed, const uint8_t *centroids, const uint16_t *scales_bf16,
-                    float *y, int32_t *acc_out, void *stream) {
-    if (!xq || !xs || !packed || !centroids || !scales_bf16 || !y)
-        return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_sizes(M, K, N);
+int64_t s3d8_tiled_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return -1;
+    return tiled_bytes(N, K);
+}
+
+int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, void *stream) {
+    if (!packed || !tiled) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_sizes(1, K, N);
     if (rc) return rc;
-    if (!aligned16(xq) || !aligned16(packed))
-        return s3d8::fail(S3D8_ERR_ALIGN, "xq and packed must be 16-byte aligned");
-    const int64_t mtiles = (M + 15) / 16;
-    if (mtiles > 65535) return s3d8::fail(S3D8_ERR_SHAPE, "M too large");
-    rc = check_device(nullptr);
+    if (tiled_bytes(N, K) > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "tiled weights over 2^31 bytes");
+    if (!aligned16(tiled)) return s3d8::fail(S3D8_ERR_ALIGN, "tiled must be 16-byte aligned");
+    int cus = 0;
+    rc = check_device(&cus);
     if (rc) return rc;
     const int64_t T = (N + 2) / 3;
     const int KB = (int)((K + 63) / 64);
-    const int kbpw = (KB + kGemvWaves - 1) / kGemvWaves;
-    dim3 grid((unsigned)((T + 15) / 16), (unsigned)mtiles);
-    hipLaunchKernelGGL(gemv_kernel, grid, dim3(kGemvThreads), 0, (hipStream_t)stream, xq, xs,
-                       (int)M, (int)K, (int)N, (int)T, packed, centroids, scales_bf16, y, acc_out,
-                       kbpw);
+    const int64_t nchunks = tiled_bytes(N, K) / 16;
+    int64_t blocks = (nchunks + kTileThreads - 1) / kTileThreads;
+    if (blocks > (int64_t)cus * 8) blocks = (int64_t)cus * 8;
+    hipLaunchKernelGGL(tile_kernel, dim3((unsigned)blocks), dim3(kTileThreads), 0, (hipStream_t)stream, packed,
+                       (int)K, (int)T, KB, nchunks, tiled);
     return launch_status();
+}
+
+namespace {
+int check_linear_args(const void *tiled, const uint8_t *centroids, const uint16_t *scales, const float *y,
+                      int64_t M, int64_t K, int64_t N) {
+    if (!tiled || !centroids || !scales || !y) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_sizes(M, K, N);
+    if (rc) return rc;
+    if (tiled_bytes(N, K) > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "tiled weights over 2^31 bytes");
+    if (!aligned16(tiled)) return s3d8::fail(S3D8_ERR_ALIGN, "tiled weights must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(centroids) & 3u)
+        return s3d8::fail(S3D8_ERR_ALIGN, "centroids must be 4-byte aligned");
+    return S3D8_OK;
+}
+}  // namespace
+
+int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
+                    float *y, int32_t *acc_out, void *stream) {
+    if (!xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    if (rc) return rc;
+    if (!aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "xq must be 16-byte aligned");
+    int cus = 0;
+    rc = check_device(&cus);
+    if (rc) return rc;
+    // the GEMV takes up to 16 token rows per launch
+    for (int64_t m0 = 0; m0 < M; m0 += 16) {
+        const int mrows = (int)(M - m0 < 16 ? M - m0 : 16);
+        GemvArgs a{xq + m0 * K, xs + m0, nullptr, nullptr, nullptr, mrows, (int)K, (int)N, (int)((N + 2) / 3),
+                   tiled, reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y + m0 * N,
+                   acc_out ? acc_out + m0 * N : nullptr};
+        if (!launch_gemv(kGemvDefault, false, a, cus, (hipStream_t)stream))
+            return s3d8::fail(S3D8_ERR_INVALID_ARG, "no GEMV variant for this launch shape");
+    }
+    return launch_status();
+}
+
+int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                     const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq, float *xs,
+                     int32_t *acc_out, void *stream) {
+    if (!x || !xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    if (rc) return rc;
+    if (!aligned16(x) || !aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "x and xq must be 16-byte aligned");
+    int cus = 0;
+    rc = check_device(&cus);
+    if (rc) return rc;
+    if (gemv_fusable((int)M, (int)K, kGemvDefault)) {
+        GemvArgs a{nullptr, nullptr, x, xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled,
+                   reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y, acc_out};
+        if (!launch_gemv(kGemvDefault, true, a, cus, (hipStream_t)stream))
+            return s3d8::fail(S3D8_ERR_INVALID_ARG, "no fused GEMV variant for this launch shape");
+        return launch_status();
+    }
+    rc = s3d8_quant_act(x, M, K, xq, xs, stream);
+    if (rc) return rc;
+    return s3d8_linear(xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, stream);
 }
 
 int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K, int8_t *w,
@@ -348,6 +719,8 @@ int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N,
     int rc = check_sizes(1, K, N);
     if (rc) return rc;
     if (!aligned16(packed) || !aligned16(w)) return s3d8::fail(S3D8_ERR_ALIGN, "packed and w must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(centroids) & 3u)
+        return s3d8::fail(S3D8_ERR_ALIGN, "centroids must be 4-byte aligned");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
@@ -357,7 +730,8 @@ int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N,
     const int64_t cap = (int64_t)cus * 2;
     if (blocks > cap) blocks = cap;
     hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0,
-                       (hipStream_t)stream, packed, centroids, (int)K, (int)N, nchunks, w);
+                       (hipStream_t)stream, packed, reinterpret_cast<const uint32_t *>(centroids), (int)K,
+                       (int)N, nchunks, w);
     return launch_status();
 }
 
