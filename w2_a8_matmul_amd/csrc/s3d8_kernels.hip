@@ -492,6 +492,281 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     }
 }
 
+// --------------------------------------------------------------- GEMM
+
+// Prefill GEMM for many token rows: INT8 activations x decoded S3D8 weights
+// on v_mfma_i32_32x32x32_i8 (INT32 accumulation).
+//
+// Workgroup tile = 128 token rows x 128 channel triples (384 output
+// channels); 4 waves side by side along N, each 128 rows x 32 triples =
+// 4 row tiles x 3 channels of the triple = 12 accumulators of 32 x 32
+// (192 AGPRs, one wave per SIMD).  Per 64-column block of K:
+//  - activations (128 x 64 INT8) and the packed weights (128 triples x 64)
+//    are copied straight from memory into LDS by buffer loads with the LDS
+//    destination bit (no registers involved), four blocks ahead of use, into
+//    a ring of five LDS slots.  The wait for a block is an explicit vmcnt
+//    count, so the loads of later blocks stay in flight;
+//  - the activation tile is stored with its 16-byte chunks XOR-swizzled by
+//    row so that the MFMA operand reads (16 rows x 16 bytes per quarter
+//    wave) hit distinct LDS banks;
+//  - each wave reads its own 2 KiB of packed weights of block kb + 1 and
+//    decodes them (LDS lookup table, see decode16) into B operands while the
+//    MFMAs of block kb run.
+// Epilogue: lane (c, h) of a 32 x 32 accumulator holds column c, i.e. the
+// three channels of triple c, for rows 8 (v / 4) + 4 h + v % 4; each row's
+// three outputs go out as one 12-byte store, 384 contiguous bytes per row and
+// half wave.
+//
+// Workgroups are mapped XCD-aware: workgroup w runs on XCD w % 8, so each
+// XCD gets a contiguous range of tiles, weight column fastest, and the tiles
+// of one XCD share their activation rows through its L2.
+constexpr int kGemmBM = 128;      // token rows per workgroup
+constexpr int kGemmBF = 8;        // weight fragments (16 triples) per workgroup
+constexpr int kGemmRT = 4;        // 32-row tiles per wave
+constexpr int kGemmSlots = 5;     // LDS ring slots
+constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
+constexpr int kXcds = 8;
+
+typedef int32_t v16i __attribute__((ext_vector_type(16)));
+
+// LDS byte offset of a __shared__ object (the value M0 takes for an
+// LDS-destination buffer load).
+#define S3D8_LDS_OFFSET(p) ((uint32_t)(size_t)((__attribute__((address_space(3))) const char *)(p)))
+
+// Buffer resource as four SGPRs for inline assembly (raw, no swizzle).
+__device__ __forceinline__ v4i rsrc_words(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    return v4i{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)bytes, kRsrcWord3};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 with the LDS bit; M0 holds the LDS base and is
+// restored afterwards).  An offset past the buffer writes zeros.  The load
+// counts in vmcnt like any vector load; the compiler does not see it, so the
+// caller waits for it explicitly.
+__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, v4i rsrc) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
+__global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                   int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
+                                                   const uint32_t *__restrict__ centroids,
+                                                   const uint16_t *__restrict__ scales, float *__restrict__ y,
+                                                   int32_t *__restrict__ acc_out, int nbm, int nbn) {
+    __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
+    __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][kGemmBM * 64];
+    __shared__ __attribute__((aligned(16))) int8_t wbuf[kGemmSlots][kGemmBF * 1024];
+    __shared__ uint32_t clw[24];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c32 = lane & 31, h = lane >> 5;
+    const int KB = (K + 63) >> 6;
+    const int tiles16 = (T + 15) >> 4;
+    const uint32_t lane_off = (uint32_t)lane << 2;
+
+    const int nwg = nbm * nbn;
+    const int per_xcd = (nwg + kXcds - 1) / kXcds;
+    const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (L >= nwg) return;  // padding workgroup (grid rounded up to a multiple of 8)
+    const int bm = L / nbn, bn = L - bm * nbn;
+    const int row0 = bm * kGemmBM;
+    const int frag0 = bn * kGemmBF + wave * 2;
+
+    uint32_t cw[24];
+#pragma unroll
+    for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+
+    const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
+    const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
+
+    // activation copy: wave w moves 16-byte units u = 64 (2 w + j) + lane of
+    // the 128 x 64 tile; unit u holds row u / 4, chunk (u % 4) ^ ((row / 4) % 4)
+    uint32_t aoff[2];
+    int acol[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = 64 * (2 * wave + j) + lane;
+        const int row = u >> 2;
+        const int chunk = (u & 3) ^ ((row >> 2) & 3);
+        aoff[j] = row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        acol[j] = 16 * chunk;
+    }
+    // weight copy: lane (c, h), k-half kh takes triple c of the wave at
+    // k = 32 kh + 16 h .. + 15, i.e. fragment lane (c % 16) + 16 (2 kh + h)
+    const int wfr = frag0 + (c32 >> 4);
+    uint32_t woff[2];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+        woff[kh] = wfr < tiles16 ? (uint32_t)wfr * (uint32_t)KB * 1024u + (uint32_t)((c32 & 15) + 16 * (2 * kh + h)) * 16u
+                                 : kOOB;
+
+    const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), wbase = S3D8_LDS_OFFSET(&wbuf[0][0]);
+    // four loads per wave and block, also for blocks past the end (they
+    // read nothing), so that every wait below counts the same
+    auto issue = [&](int kb, int slot) {
+        const bool live = kb < KB;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            load_to_lds16(abase + (uint32_t)(kGemmBM * 64) * slot + 1024u * (2 * wave + j),
+                          (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+            load_to_lds16(wbase + (uint32_t)(kGemmBF * 1024) * slot + 2048u * wave + 1024u * kh,
+                          (live && woff[kh] != kOOB) ? woff[kh] + 1024u * kb : kOOB, rw);
+    };
+
+    // A operand of row tile i, k-half kh: row 32 i + c32, chunk 2 kh + h
+    const int swz = (c32 >> 2) & 3;
+    const int ard0 = c32 * 64 + 16 * (h ^ swz), ard1 = c32 * 64 + 16 * ((h ^ swz) ^ 2);
+
+    // decode dword c of k-half kh of the raw weights into operand set bs
+    auto decode_piece = [&](const uint4 (&ps)[2], v4i (&bs)[2][3], int kh, int c) {
+        const char *tb = reinterpret_cast<const char *>(tab);
+        const uint32_t dw = c == 0 ? ps[kh].x : c == 1 ? ps[kh].y : c == 2 ? ps[kh].z : ps[kh].w;
+        const uint32_t a0 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0400u);
+        const uint32_t a1 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0500u);
+        const uint32_t a2 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0600u);
+        const uint32_t a3 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0700u);
+        const uint32_t q0 = *reinterpret_cast<const uint32_t *>(tb + a0);
+        const uint32_t q1 = *reinterpret_cast<const uint32_t *>(tb + a1);
+        const uint32_t q2 = *reinterpret_cast<const uint32_t *>(tb + a2);
+        const uint32_t q3 = *reinterpret_cast<const uint32_t *>(tb + a3);
+        const uint32_t p01 = __builtin_amdgcn_perm(q1, q0, 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(q3, q2, 0x05010400u);
+        const uint32_t s01 = __builtin_amdgcn_perm(q1, q0, 0x0C0C0602u);
+        const uint32_t s23 = __builtin_amdgcn_perm(q3, q2, 0x0C0C0602u);
+        bs[kh][0][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        bs[kh][1][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        bs[kh][2][c] = (int32_t)__builtin_amdgcn_perm(s23, s01, 0x05040100u);
+    };
+    auto read_w = [&](uint4 (&ps)[2], int slot) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+            ps[kh] = *reinterpret_cast<const uint4 *>(&wbuf[slot][2048 * wave + 1024 * kh + 16 * lane]);
+    };
+
+    // prologue: blocks 0 .. kGemmAhead - 1 in flight, build the table
+#pragma unroll
+    for (int s = 0; s < kGemmAhead; ++s) issue(s, s);
+    if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    }
+    __syncthreads();
+    {
+        const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
+        for (int idx = tid; idx < kTabWords / 4; idx += 256) {
+            const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+            reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+        }
+    }
+    static_assert(kGemmAhead == 4, "the vmcnt immediates below assume four blocks in flight");
+    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // this wave's block 0 is in LDS
+    __syncthreads();                                    // everyone's block 0, and the table
+
+    v16i acc[kGemmRT][3];
+#pragma unroll
+    for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) acc[i][d] = v16i{};
+
+    v4i b0[2][3], b1[2][3];
+    {
+        uint4 w0[2];
+        read_w(w0, 0);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) decode_piece(w0, b0, kh, c);
+    }
+
+    // block kb (LDS slot `slot`): wait until blocks <= kb + 1 are in LDS for
+    // every wave (8 loads = blocks kb + 2, kb + 3 may stay in flight), refill
+    // the slot of block kb - 1 with block kb + 4, then MFMAs of A(kb) x bc
+    // with the decode of W(kb + 1) into bnx between them
+    auto block = [&](const v4i (&bc)[2][3], v4i (&bnx)[2][3], int kb, int slot) {
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int next = slot == kGemmSlots - 1 ? 0 : slot + 1;
+        const int prev = slot == 0 ? kGemmSlots - 1 : slot - 1;
+        issue(kb + kGemmAhead, prev);
+        const int8_t *ab = abuf[slot];
+        v4i a[kGemmRT][2];
+#pragma unroll
+        for (int i = 0; i < kGemmRT; ++i) {
+            a[i][0] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard0);
+            a[i][1] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard1);
+        }
+        uint4 wn[2];
+        read_w(wn, next);
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < kGemmRT; ++i) {
+#pragma unroll
+                for (int d = 0; d < 3; ++d)
+                    acc[i][d] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][kh], bc[kh][d], acc[i][d], 0, 0, 0);
+                decode_piece(wn, bnx, kh, i);
+            }
+    };
+
+    int kb = 0, slot = 0;
+#pragma unroll 1
+    for (; kb + 1 < KB; kb += 2) {
+        block(b0, b1, kb, slot);
+        slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
+        block(b1, b0, kb + 1, slot);
+        slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
+    }
+    if (kb < KB) block(b0, b1, kb, slot);
+    // loads of blocks past the end are still in flight: drain before exit
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // epilogue: y = (xs[row] * acc) * alpha[ch], channel 3 (16 frag0 + c) + d
+    const int ch0 = 3 * (16 * frag0 + c32);
+    float sc[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) sc[d] = ch0 + d < N ? bf16_to_f32(scales[ch0 + d]) : 0.0f;
+    const bool full = ch0 + 2 < N;
+    typedef float f3u __attribute__((ext_vector_type(3))) __attribute__((aligned(4)));
+#pragma unroll
+    for (int i = 0; i < kGemmRT; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (row >= M) continue;
+            const float sx = xs[row];
+            float o[3];
+#pragma unroll
+            for (int d = 0; d < 3; ++d) o[d] = (sx * (float)acc[i][d][v]) * sc[d];
+            float *dst = y + (int64_t)row * N + ch0;
+            if (full) {
+                *reinterpret_cast<f3u *>(dst) = f3u{o[0], o[1], o[2]};
+            } else {
+#pragma unroll
+                for (int d = 0; d < 3; ++d)
+                    if (ch0 + d < N) dst[d] = o[d];
+            }
+            if (acc_out) {
+                int32_t *da = acc_out + (int64_t)row * N + ch0;
+#pragma unroll
+                for (int d = 0; d < 3; ++d)
+                    if (ch0 + d < N) da[d] = acc[i][d][v];
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------------- dequant
 
 // Standalone S3D8 -> channel-INT8 decode (the blog's dequantisation kernel).
@@ -679,6 +954,18 @@ int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
+    if (M > 16) {
+        const int64_t T = (N + 2) / 3;
+        const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
+        const int nbn = (int)(((T + 15) / 16 + kGemmBF - 1) / kGemmBF);
+        const int64_t nwg = (int64_t)nbm * nbn;
+        const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
+        if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
+        hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M,
+                           (int)K, (int)N, (int)T, tiled, reinterpret_cast<const uint32_t *>(centroids),
+                           scales_bf16, y, acc_out, nbm, nbn);
+        return launch_status();
+    }
     // the GEMV takes up to 16 token rows per launch
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
         const int mrows = (int)(M - m0 < 16 ? M - m0 : 16);
