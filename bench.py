@@ -66,20 +66,27 @@ def measured_traffic(name, launches_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
-def per_kernel_us(torch, fn, n, spin_cycles=50_000_000):
-    """Average GPU duration of fn() (one kernel launch) from events around
-    each launch.  A spin kernel queued first holds the stream until every
-    launch and event is queued, so host gaps do not enter the intervals."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+def graph_launch_us(torch, fns, reps):
+    """Average duration of one launch: the launches fns[0..n-1] (one kernel
+    each) are captured back to back in one HIP graph, replayed `reps` times
+    between two events on the launching stream; the interval over n * reps
+    launches includes no host time, only the kernels and the gaps between
+    consecutive dispatches."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
     torch.cuda.synchronize()
-    torch.cuda._sleep(spin_cycles)
-    for i in range(n):
-        ev[i][0].record()
-        fn(i)
-        ev[i][1].record()
+    g.replay()
     torch.cuda.synchronize()
-    d = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    return float(d.mean()), float(np.median(d))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(fns))
 
 
 def main():
@@ -172,13 +179,15 @@ def main():
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
 
     # dominant kernel: the fused quantise + decode GEMV launched by
-    # s3d8_forward (the whole step at M=1), its own duration
-    lin_mean_us, lin_med_us = per_kernel_us(torch, lambda i: step(i % R), 4 * R)
-    qa_mean_us, _ = per_kernel_us(torch, lambda i: s3d8.quant_act(dX[i % R], xq, xsc), 2 * R)
+    # s3d8_forward.  At M=1 a step is exactly one launch of it, so its
+    # average duration is the timed region over the launches in it.
+    lin_mean_us = ms_per_step * 1e3
     achieved = kernel_bytes / (lin_mean_us * 1e-6) / 1e9
     traffic = measured_traffic("gemv_c1_m1", kernel_bytes)
+    # standalone quantisation kernel (used by s3d8_linear callers), for reference
+    qa_mean_us = graph_launch_us(torch, [lambda r=r: s3d8.quant_act(dX[r], xq, xsc) for r in range(R)], 10)
     log(f"step {ms_per_step * 1e3:.2f} us -> {value:.1f} GB/s; forward kernel {lin_mean_us:.2f} us "
-        f"(median {lin_med_us:.2f}) -> {achieved:.1f} GB/s; quant_act {qa_mean_us:.2f} us")
+        f"-> {achieved:.1f} GB/s; quant_act alone {qa_mean_us:.2f} us")
     del dP, dX
 
     # ---------------------------------------------------------------- prefill GEMM
@@ -202,9 +211,8 @@ def main():
         for i in range(2):
             s3d8.linear(xqp, xsp, dPp[i % Rp], dCp, dSp, lp.N, y=yp)
         torch.cuda.synchronize()
-        nrep = 20
-        g_mean_us, g_med_us = per_kernel_us(
-            torch, lambda i: s3d8.linear(xqp, xsp, dPp[i % Rp], dCp, dSp, lp.N, y=yp), nrep)
+        g_mean_us = graph_launch_us(
+            torch, [lambda r=r: s3d8.linear(xqp, xsp, dPp[r], dCp, dSp, lp.N, y=yp) for r in range(Rp)], 5)
         ops = 2.0 * lp.M * lp.K * lp.N
         tops = ops / (g_mean_us * 1e-6) / 1e12
         log(f"prefill GEMM {lp.name}: {g_mean_us:.1f} us -> {tops:.1f} TOPS")
