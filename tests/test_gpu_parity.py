@@ -305,3 +305,41 @@ def test_forward_gate_up_m1(gpu):
     np.testing.assert_array_equal(xq, xq_r)
     np.testing.assert_array_equal(acc, acc_r)
     check_y(y, y_r)
+
+
+def _half_integer_rows(K):
+    """Rows whose quotients x / s sit on or one ulp beside k + 1/2: the fused
+    quantiser's fast path must hand these to the exact division."""
+    k = (np.arange(K) % 254) - 127                     # -127 .. 126
+    half = (k + 0.5).astype(np.float32)
+    rows = np.zeros((4, K), np.float32)
+    rows[0] = half                                      # s = 1 exactly: x / s = k + 1/2
+    rows[0, 0] = 127.0
+    s = np.float32(np.float32(300.0) / np.float32(127.0))
+    v = (half * s).astype(np.float32)                   # x / s within an ulp of k + 1/2
+    rows[1] = np.where(np.arange(K) % 3 == 0, np.nextafter(v, np.float32(np.inf)),
+                       np.where(np.arange(K) % 3 == 1, np.nextafter(v, np.float32(-np.inf)), v))
+    rows[1, 1] = 300.0
+    tiny = np.float32(2.0 ** -149)
+    rows[2, :4] = [tiny * np.float32(100), tiny * np.float32(3), -tiny * np.float32(50), tiny * np.float32(25)]
+    rows[3] = workloads.gaussian_matrix([2060, K], 1, K)[0]
+    return rows
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("K", [1040, 4096])
+def test_forward_quantiser_rounding_boundaries(gpu, M, K):
+    """The fused (one-launch) path quantises with a reciprocal and falls back
+    to the IEEE quotient near rounding boundaries: codes must still equal
+    the oracle's rne(x / s) for every element."""
+    N = 97
+    C, alpha, packed = random_format([2061, M, K], N, K)
+    rows = _half_integer_rows(K)
+    for first in range(4):
+        x = np.ascontiguousarray(np.roll(rows, -first, axis=0)[:M])
+        xq, xs, acc, y = run_forward(x, C, alpha, packed, N, gpu)
+        xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+        np.testing.assert_array_equal(xs, xs_r)
+        np.testing.assert_array_equal(xq, xq_r)
+        np.testing.assert_array_equal(acc, acc_r)
+        check_y(y, y_r)

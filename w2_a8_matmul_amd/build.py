@@ -22,6 +22,9 @@ HIP_FLAGS = [
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
     # no packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first kernel arguments arrive in SGPRs at wave start (gfx950
+    # kernarg preload) instead of through a scalar load round trip
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I", INCLUDE, "-I", CSRC,
 ]
 HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-march=x86-64-v3", "-ffp-contract=off",

@@ -93,6 +93,34 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// LDS byte offset of a __shared__ object (the value M0 takes for an
+// LDS-destination buffer load).
+#define S3D8_LDS_OFFSET(p) ((uint32_t)(size_t)((__attribute__((address_space(3))) const char *)(p)))
+
+// Buffer resource as four SGPRs for inline assembly (raw, no swizzle).
+__device__ __forceinline__ v4i rsrc_words(const void *p, uint32_t bytes) {
+    const uint64_t a = (uint64_t)p;
+    return v4i{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)bytes, kRsrcWord3};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane
+// (buffer_load_dwordx4 with the LDS bit; M0 holds the LDS base and is
+// restored afterwards).  An offset past the buffer writes zeros.  The load
+// counts in vmcnt like any vector load; the compiler does not see it, so the
+// caller waits for it explicitly.
+__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, v4i rsrc) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "memory");
+}
+
 // Stage the 96-byte centroid table (read through the scalar cache, so it does
 // not queue behind the vector loads already in flight) into LDS, then build
 // the lane-interleaved signed table.  C32 must be 4-byte aligned.  Contains
@@ -492,6 +520,329 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     }
 }
 
+// --------------------------------------------------------------- streaming fused GEMV
+
+// Quantise + decode GEMV for 1..4 token rows, the weight stream started at
+// kernel entry.
+//
+// At one token the layer is a single read of the packed matrix; what limits
+// it is how early that read starts, how long the chain in front of the first
+// decode is, and how evenly the bytes are spread.  Every wave issues, before
+// anything else, one load of the centroid row its lanes need for the table,
+// its share of the fp32 activations, and its first kStreamSlots weight
+// fragments (1 KiB each, buffer loads straight into a private LDS ring, no
+// registers).  The table is then built from registers, the row absmax is
+// reduced with DPP, and one barrier later the activations are quantised and
+// the decode starts.  The main loop has no barriers: each wave waits for its
+// own ring slot (an explicit vmcnt count: the compiler does not see these
+// loads), decodes it, runs three v_mfma_i32_16x16x64_i8 (token rows as the A
+// operand, rows >= M read a zero block) and refills the slot four fragments
+// ahead.
+//
+// Work split: a workgroup takes tiles of 16 triples (blockIdx.x, + grid,
+// ...), its 16 waves split K into ranges of kbw 64-column blocks.  Partial
+// sums of a tile meet in LDS through integer atomics (exact, order-free) and
+// stay there until the end; every global store (y, the optional
+// accumulators, xq and xs) happens after the last weight load has landed, so
+// no store enters the vmcnt counts.
+constexpr int kStreamWaves = 16;
+constexpr int kStreamSlots = 4;      // ring slots (1 KiB fragments) per wave
+constexpr int kStreamMaxTiles = 16;  // tiles per workgroup (results held in LDS)
+constexpr int kStreamEp = kStreamMaxTiles * kFusedMaxRows * 48 / (kStreamWaves * 64);  // outputs per thread
+
+// max over each row of 16 lanes, result in every lane of the row (DPP:
+// swap neighbours, swap pairs, mirror halves of 8, mirror the row)
+__device__ __forceinline__ float row16_max(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+// max over the wave, wave-uniform
+__device__ __forceinline__ float wave_max(float v) {
+    v = row16_max(v);
+    const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
+    const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+    return fmaxf(a, b);
+}
+
+// Arguments used before the first loads come first, so that they are among
+// the kernel arguments preloaded into SGPRs.
+__global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
+    const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
+    const uint16_t *__restrict__ scales, int M, int K, int N, int T, int kbw, int grid, float *__restrict__ y,
+    int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    constexpr int kThreads = kStreamWaves * 64;
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+    __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kStreamWaves][kStreamSlots][1024];
+    __shared__ __attribute__((aligned(16))) int8_t xw[kStreamWaves][1024];
+    __shared__ __attribute__((aligned(16))) int8_t zero16[16];
+    __shared__ int32_t ybuf[kStreamMaxTiles * kFusedMaxRows * 48];
+    __shared__ float rmax[kStreamWaves * kFusedMaxRows];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int KB = (K + 63) >> 6;
+    const int tiles = (T + 15) >> 4;
+    const int kb0 = wave * kbw;
+    const int ntw = (tiles - (int)blockIdx.x + grid - 1) / grid;  // tiles of this workgroup, >= 1
+    const int nout = ntw * M * 48;                                 // outputs of this workgroup
+
+    // 1. epilogue scales (the compiler's loads, issued first: the explicit
+    //    vmcnt counts below never wait for them).  Output idx = tid + q *
+    //    kThreads is (tile j, row r, channel c), j = idx / (48 M).
+    const uint32_t invM = 0x10000u / (uint32_t)M + 1u;  // (x * invM) >> 16 == x / M for x < 64
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales, (uint32_t)N * 2u);
+    uint16_t ep_a[kStreamEp];
+    int ep_j[kStreamEp], ep_r[kStreamEp], ep_c[kStreamEp];
+#pragma unroll
+    for (int q = 0; q < kStreamEp; ++q) {
+        const int idx = tid + q * kThreads;
+        const int i48 = idx / 48, c = idx - 48 * i48;
+        const int j = (int)(((uint32_t)i48 * invM) >> 16), r = i48 - j * M;
+        ep_j[q] = j;
+        ep_r[q] = r;
+        ep_c[q] = c;
+        const int ch = ((int)blockIdx.x + j * grid) * 48 + c;
+        ep_a[q] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (idx < nout && ch < N) ? (uint32_t)ch * 2u : kOOB, 0, 0);
+    }
+
+    // 2. the centroid rows of this thread's table entries: entry b = idx / 16
+    //    of uint4 idx = tid + kThreads i uses row (b / 2) % 32, which takes
+    //    kCenRows distinct values per thread (8 bytes from a 4-aligned
+    //    offset inside the 96-byte table each)
+    constexpr int kCenRows = 1024 / kThreads;
+    const v4i rcen = rsrc_words(centroids, 96u);
+    u2v cpair[kCenRows];
+    int cshift[kCenRows];
+#pragma unroll
+    for (int k = 0; k < kCenRows; ++k) {
+        const int qrow = ((tid >> 5) + k * (kThreads >> 5)) & 31;
+        const int cbase = min((3 * qrow) & ~3, 88);
+        cshift[k] = 8 * (3 * qrow - cbase);
+        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(cpair[k]) : "v"((uint32_t)cbase), "s"(rcen) : "memory");
+    }
+
+    // 3. activations: this wave's K range of every row, up to 4 float4 per
+    //    lane; float4 f of the range is row f / (16 kbw)
+    const v4i rx = rsrc_words(xf, (uint32_t)M * (uint32_t)K * 4u);
+    const int span4 = 16 * kbw;
+    const int nf4 = (M * span4 + 63) >> 6;  // float4 per lane in use (<= 4)
+    f4v xv[kFusedXF4];
+    int xm[kFusedXF4], xr[kFusedXF4];
+#pragma unroll
+    for (int i = 0; i < kFusedXF4; ++i) {
+        const int f = lane + 64 * i;
+        const int m = (f >= span4) + (f >= 2 * span4) + (f >= 3 * span4) + (f >= 4 * span4);
+        const int r = f - m * span4;
+        xm[i] = m;
+        xr[i] = r;
+        // unconditional: a register written by these loads must not pass
+        // through a branch merge (the compiler would copy it before it lands)
+        const int k = kb0 * 64 + 4 * r;
+        const uint32_t off = (i < nf4 && m < M && k < K) ? ((uint32_t)m * (uint32_t)K + (uint32_t)k) * 4u : kOOB;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(xv[i]) : "v"(off), "s"(rx) : "memory");
+    }
+
+    // every wave's small loads enter the CU's memory queue before any
+    // fragment load does
+    asm volatile("s_barrier" ::: "memory");
+
+    // 4. weight fragments: step s of this wave = tile j = s / kbw of the
+    //    workgroup, block kb0 + s % kbw; steps past the end read nothing
+    const v4i rw = rsrc_words(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
+    const uint32_t ring_base = S3D8_LDS_OFFSET(&ring[wave][0][0]);
+    int is_j = 0, is_b = 0;  // (tile, block) of the next step to issue
+    auto issue_next = [&](int slot) {
+        const int kb = kb0 + is_b;
+        const bool live = is_j < ntw && kb < KB;
+        const uint32_t tile = (uint32_t)((int)blockIdx.x + is_j * grid);
+        load_to_lds16(ring_base + 1024u * slot,
+                      live ? (tile * (uint32_t)KB + (uint32_t)kb) * 1024u + (uint32_t)lane * 16u : kOOB, rw);
+        if (++is_b == kbw) {
+            is_b = 0;
+            ++is_j;
+        }
+    };
+#pragma unroll
+    for (int sl = 0; sl < kStreamSlots; ++sl) issue_next(sl);
+
+    for (int i = tid; i < kStreamMaxTiles * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
+    if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
+
+    // table: entry b holds [w0, w1, w2, 0] with w_d = +-C[q][d], q = (b >> 1)
+    // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0
+    static_assert(kCenRows == 1 || kCenRows == 2, "one or two centroid rows per thread");
+    if constexpr (kCenRows == 1) {
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    }
+#pragma unroll
+    for (int i = 0; i < kTabWords / 4 / kThreads; ++i) {
+        const int idx = tid + kThreads * i;
+        const int b = idx >> 4, k = i % kCenRows;
+        const uint64_t cv = (((uint64_t)cpair[k].y << 32) | cpair[k].x) >> cshift[k];
+        const int32_t c0 = (int32_t)(cv & 0xFF), c1 = (int32_t)((cv >> 8) & 0xFF), c2 = (int32_t)((cv >> 16) & 0xFF);
+        const int s0 = b & 1, s1 = (b >> 6) & 1, s2 = ((b >> 7) ^ b) & 1;
+        const uint32_t v = (uint32_t)((s0 ? -c0 : c0) & 0xFF) | ((uint32_t)((s1 ? -c1 : c1) & 0xFF) << 8) |
+                           ((uint32_t)((s2 ? -c2 : c2) & 0xFF) << 16);
+        reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+    }
+
+    // activations landed (only fragment loads behind them)
+    asm volatile("s_waitcnt vmcnt(%4)"
+                 : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3])
+                 : "n"(kStreamSlots)
+                 : "memory");
+#pragma unroll
+    for (int r = 0; r < kFusedMaxRows; ++r) {
+        if (r < M) {  // uniform
+            float a = 0.0f;
+#pragma unroll
+            for (int i = 0; i < kFusedXF4; ++i)
+                if (i < nf4 && xm[i] == r)
+                    a = fmaxf(a, fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w))));
+            a = wave_max(a);
+            if (lane == 0) rmax[wave * kFusedMaxRows + r] = a;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table, rmax, ybuf complete
+
+    // per-token scale s = a / 127 (lane w of each row reads wave w's maximum),
+    // codes clamp(rne(x / s), -127, 127) into this wave's slice of xw
+    float srow[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < kFusedMaxRows; ++r) {
+        if (r < M) {  // uniform
+            const float a = row16_max(n < kStreamWaves ? rmax[n * kFusedMaxRows + r] : 0.0f);
+            srow[r] = (a == 0.0f) ? 0.0f : a / 127.0f;
+        }
+    }
+    // rne(x / s) through t = x * rcp(s), rcp the hardware reciprocal (error
+    // below 1 ulp): |t - x / s| < 2.5e-7 |x / s| <= 3.2e-5, so whenever t is
+    // more than 1e-4 away from a half-integer, t, the exact quotient and its
+    // fp32 rounding lie in the same rounding interval and rint(t) is the
+    // code; otherwise (and for a tiny s) the IEEE quotient decides.
+    float rcp[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int r = 0; r < kFusedMaxRows; ++r)
+        if (r < M) rcp[r] = srow[r] >= 1e-30f ? __builtin_amdgcn_rcpf(srow[r]) : 0.0f;
+    auto code = [](float xe, float sc, float rc) {
+        float q;
+        const float t = xe * rc;
+        const float qt = rintf(t);
+        if (rc != 0.0f && fabsf(fabsf(t - qt) - 0.5f) > 1e-4f) {
+            q = qt;
+        } else {
+            q = rintf(xe / sc);
+        }
+        return (signed char)fminf(127.0f, fmaxf(-127.0f, q));
+    };
+#pragma unroll
+    for (int i = 0; i < kFusedXF4; ++i) {
+        if (i < nf4 && xm[i] < M) {
+            float sc = srow[0], rc = rcp[0];
+#pragma unroll
+            for (int rr = 1; rr < kFusedMaxRows; ++rr) {
+                sc = (xm[i] == rr) ? srow[rr] : sc;
+                rc = (xm[i] == rr) ? rcp[rr] : rc;
+            }
+            char4 o = make_char4(0, 0, 0, 0);
+            if (sc != 0.0f) {
+                o.x = code(xv[i].x, sc, rc);
+                o.y = code(xv[i].y, sc, rc);
+                o.z = code(xv[i].z, sc, rc);
+                o.w = code(xv[i].w, sc, rc);
+            }
+            *reinterpret_cast<char4 *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]) = o;
+        }
+    }
+
+    // A operand: rows < M read their codes (advancing 64 bytes per block),
+    // the other lanes a zero block
+    const int8_t *xa = n < M ? &xw[wave][n * 64 * kbw + g * 16] : zero16;
+    const int xa_step = n < M ? 64 : 0;
+    const uint32_t lane_off = (uint32_t)lane << 2;
+    const int nsteps = ntw * kbw;  // fragments per wave
+
+    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+    int slot = 0, bl = 0, j = 0;
+#pragma unroll 1
+    for (int st = 0; st < nsteps; ++st) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStreamSlots - 1) : "memory");  // this step's fragment landed
+        const uint4 p = *reinterpret_cast<const uint4 *>(&ring[wave][slot][16 * lane]);
+        const v4i a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot read: it may be refilled
+        issue_next(slot);
+        v4i b0, b1, b2;
+        decode16(p, lane_off, tab, b0, b1, b2);
+        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b2, acc2, 0, 0, 0);
+        slot = slot == kStreamSlots - 1 ? 0 : slot + 1;
+        if (++bl == kbw) {
+            // tile j done for this wave: rows 0..3 sit in lanes 0..15 (g = 0),
+            // element r; channel of (col n, d) within the tile is 3n + d
+            if (g == 0 && kb0 < KB) {
+#pragma unroll
+                for (int r = 0; r < kFusedMaxRows; ++r) {
+                    if (r < M) {
+                        int32_t *yb = &ybuf[(j * kFusedMaxRows + r) * 48 + 3 * n];
+                        atomicAdd(yb + 0, acc0[r]);
+                        atomicAdd(yb + 1, acc1[r]);
+                        atomicAdd(yb + 2, acc2[r]);
+                    }
+                }
+            }
+            acc0 = v4i{0, 0, 0, 0};
+            acc1 = v4i{0, 0, 0, 0};
+            acc2 = v4i{0, 0, 0, 0};
+            bl = 0;
+            ++j;
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    // epilogue
+#pragma unroll
+    for (int q = 0; q < kStreamEp; ++q) {
+        const int jj = ep_j[q], r = ep_r[q], c = ep_c[q];
+        const int ch = ((int)blockIdx.x + jj * grid) * 48 + c;
+        if (jj < ntw && ch < N) {
+            float sx = srow[0];
+#pragma unroll
+            for (int rr = 1; rr < kFusedMaxRows; ++rr) sx = (r == rr) ? srow[rr] : sx;
+            const int32_t sum = ybuf[(jj * kFusedMaxRows + r) * 48 + c];
+            y[(int64_t)r * N + ch] = (sx * (float)sum) * bf16_to_f32(ep_a[q]);
+            if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
+        }
+    }
+    if (blockIdx.x == 0) {
+        if (tid < M && xs_out) {
+            float sx = srow[0];
+#pragma unroll
+            for (int rr = 1; rr < kFusedMaxRows; ++rr) sx = (tid == rr) ? srow[rr] : sx;
+            xs_out[tid] = sx;
+        }
+        if (xq_out) {
+#pragma unroll
+            for (int i = 0; i < kFusedXF4; ++i) {
+                const int k = kb0 * 64 + 4 * xr[i];
+                if (i < nf4 && xm[i] < M && k < K)
+                    *reinterpret_cast<char4 *>(xq_out + (int64_t)xm[i] * K + k) =
+                        *reinterpret_cast<const char4 *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]);
+            }
+        }
+    }
+}
+
 // --------------------------------------------------------------- GEMM
 
 // Prefill GEMM for many token rows: INT8 activations x decoded S3D8 weights
@@ -528,34 +879,6 @@ constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
 constexpr int kXcds = 8;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
-
-// LDS byte offset of a __shared__ object (the value M0 takes for an
-// LDS-destination buffer load).
-#define S3D8_LDS_OFFSET(p) ((uint32_t)(size_t)((__attribute__((address_space(3))) const char *)(p)))
-
-// Buffer resource as four SGPRs for inline assembly (raw, no swizzle).
-__device__ __forceinline__ v4i rsrc_words(const void *p, uint32_t bytes) {
-    const uint64_t a = (uint64_t)p;
-    return v4i{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)bytes, kRsrcWord3};
-}
-
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 with the LDS bit; M0 holds the LDS base and is
-// restored afterwards).  An offset past the buffer writes zeros.  The load
-// counts in vmcnt like any vector load; the compiler does not see it, so the
-// caller waits for it explicitly.
-__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, v4i rsrc) {
-    uint32_t saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds), "v"(voff), "s"(rsrc)
-        : "memory");
-}
 
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
@@ -889,6 +1212,25 @@ bool launch_gemv(GemvConfig cfg, bool fused, const GemvArgs &a, int cus, hipStre
 
 int64_t tiled_bytes(int64_t N, int64_t K) { return ((N + 2) / 3 + 15) / 16 * ((K + 63) / 64) * 1024; }
 
+// The streaming fused GEMV takes M <= 4 rows whose per-wave activation slice
+// fits four float4 per lane, and at most kStreamMaxTiles tiles per workgroup
+// (one workgroup per CU).  Returns false (launching nothing) otherwise.
+bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_t K, int64_t N,
+                        const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, float *y,
+                        int32_t *acc_out, int cus, hipStream_t stream) {
+    if (M < 1 || M > kFusedMaxRows) return false;
+    const int kbw = gemv_kbw((int)K, kStreamWaves);
+    if (M * kbw > 16) return false;
+    const int64_t T = (N + 2) / 3;
+    const int64_t tiles = (T + 15) / 16;
+    const int64_t grid = tiles < cus ? tiles : cus;
+    if ((tiles + grid - 1) / grid > kStreamMaxTiles) return false;
+    hipLaunchKernelGGL(gemv_stream_kernel, dim3((unsigned)grid), dim3(kStreamWaves * 64), 0, stream, x, tiled,
+                       centroids, scales, (int)M, (int)K, (int)N, (int)T, kbw,
+                       (int)grid, y, acc_out, xq, xs);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -988,6 +1330,8 @@ int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
+    if (launch_gemv_stream(x, xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, cus, (hipStream_t)stream))
+        return launch_status();
     if (gemv_fusable((int)M, (int)K, kGemvDefault)) {
         GemvArgs a{nullptr, nullptr, x, xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled,
                    reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y, acc_out};
