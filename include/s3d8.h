@@ -193,6 +193,33 @@ int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint
                      const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq,
                      float *xs, int32_t *acc_out, void *stream);
 
+/* Size in bytes of the workspace of s3d8_linear_unfused: the whole matrix
+ * decoded to channel-INT8 in 2 KiB fragments of 32 channels x 64 columns,
+ * ceil(3 * ceil(N/3) / 32) * ceil(K/64) * 2048.  -1 on bad sizes. */
+int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K);
+
+/* The linear layer of s3d8_linear computed the way the blog's CPU kernels
+ * treat more than one token ("Fast? How fast?": dequantise to INT8, then an
+ * INT8 matrix product): the tiled matrix is decoded once into `workspace`
+ * as channel-INT8, then an INT8 x INT8 GEMM with INT32
+ * accumulation and the same fp32 epilogue runs on it.  Results are
+ * identical to s3d8_linear; for many token rows it decodes each weight once
+ * per call instead of once per row tile.  (The workspace layout is
+ * internal to the library.)
+ *   xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out
+ *                as for s3d8_linear.
+ *   workspace    device scratch, 16-B aligned, at least
+ *                s3d8_unfused_workspace_bytes(N, K) bytes, owned by the
+ *                caller; overwritten.  Calls that may run concurrently
+ *                need separate workspaces.
+ *   workspace_bytes  its size.
+ * Errors: INVALID_ARG (also a workspace too small), SHAPE (decoded matrix
+ * over 2^31 bytes), ALIGN, DEVICE, HIP. */
+int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
+                            float *y, int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes,
+                            void *stream);
+
 /* Decode a whole matrix to channel-INT8 ([PAPER] Eq. 1 without alpha; the
  * blog's standalone S3D8 -> INT8 dequantisation).
  *   packed     device uint8 [ceil(N/3)][K], 16-B aligned.

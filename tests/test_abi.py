@@ -129,6 +129,28 @@ def test_dequant_validation():
     assert L.s3d8_dequant(A16, A16, 0, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
 
 
+def test_linear_unfused_validation():
+    L = _lib.lib()
+    assert L.s3d8_unfused_workspace_bytes(10, 64) == 2048  # 12 channels: one 32-channel fragment
+    assert L.s3d8_unfused_workspace_bytes(14336, 4096) == 449 * 64 * 2048
+    assert L.s3d8_unfused_workspace_bytes(0, 64) == -1
+    need = L.s3d8_unfused_workspace_bytes(9, 64)
+
+    def call(ws=A16, nbytes=need, xq=A16, K=64):
+        return L.s3d8_linear_unfused(xq, A16, 1, K, 9, A16, A16, A16, A16, None, ws, nbytes, None)
+
+    assert call(ws=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(nbytes=need - 1) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(ws=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(xq=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(K=24) == _lib.S3D8_ERR_SHAPE
+    assert call(nbytes=need - 1) == _lib.S3D8_ERR_INVALID_ARG
+    assert b"workspace" in L.s3d8_last_error()
+    # a decoded matrix over 2^31 bytes is refused before any device work
+    assert L.s3d8_linear_unfused(A16, A16, 1, 16384, 400000, A16, A16, A16, A16, None, A16, 1 << 40,
+                                 None) == _lib.S3D8_ERR_SHAPE
+
+
 def test_host_validation_errors():
     W = np.zeros((3, 16), np.float32)
     with pytest.raises(s3d8.S3D8Error) as e:

@@ -50,12 +50,12 @@ def relayout(packed, K):
     return P.reshape(tiles, 16, KB, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
 
 
-def run_linear(x, C, alpha, packed, N, device):
+def run_linear(x, C, alpha, packed, N, device, unfused=False):
     xd = dev(x, device)
     xq, xs = s3d8.quant_act(xd)
     tiled = s3d8.tile(dev(packed, device), N)
-    y, acc = s3d8.linear(xq, xs, tiled, dev(C, device), dev(alpha.view(np.int16), device), N,
-                         return_acc=True)
+    fn = s3d8.linear_unfused if unfused else s3d8.linear
+    y, acc = fn(xq, xs, tiled, dev(C, device), dev(alpha.view(np.int16), device), N, return_acc=True)
     torch.cuda.synchronize()
     return xq.cpu().numpy(), xs.cpu().numpy(), acc.cpu().numpy(), y.cpu().numpy()
 
@@ -208,10 +208,10 @@ def _full_compare(lin, gpu, M=None):
     check_y(y, y_r)
 
 
-def _sampled_compare(lin, gpu, nsamples=512):
+def _sampled_compare(lin, gpu, nsamples=512, unfused=False):
     C, alpha, packed = packed_matrix(lin)
     x = workloads.activations(lin)
-    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu, unfused=unfused)
     xq_r, xs_r = oracle.quant_act(x)
     np.testing.assert_array_equal(xq, xq_r)
     np.testing.assert_array_equal(xs, xs_r)
@@ -343,3 +343,71 @@ def test_forward_quantiser_rounding_boundaries(gpu, M, K):
         np.testing.assert_array_equal(xq, xq_r)
         np.testing.assert_array_equal(acc, acc_r)
         check_y(y, y_r)
+
+
+# ------------------------------------------------------------------ unfused prefill path
+@pytest.mark.parametrize("M,K,N", FUZZ)
+def test_linear_unfused_shape_fuzz(gpu, M, K, N):
+    """s3d8_linear_unfused (decode to an INT8 workspace, then INT8 GEMM) on
+    the same ragged shapes as the fused path."""
+    C, alpha, packed = random_format([2020, M, K, N], N, K)
+    x = workloads.gaussian_matrix([2021, M, K], M, K)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu, unfused=True)
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+def test_linear_unfused_extremes_and_zeros(gpu):
+    K, N = 14336, 6
+    C = np.full((32, 3), 127, np.uint8)
+    packed = np.zeros((2, K), np.uint8)
+    packed[0, :] = 0x3E
+    packed[1, :] = 0x7F
+    alpha = oracle.f32_to_bf16(np.full(6, 1.0, np.float32))
+    x = np.full((3, K), 3.0, np.float32)
+    x[1] *= -1
+    x[2] = 0
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu, unfused=True)
+    big = K * 127 * 127
+    assert acc.tolist() == [[big] * 3 + [-big] * 3, [-big] * 3 + [big] * 3, [0] * 6]
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    check_y(y, y_r)
+
+
+def test_linear_unfused_prefill_gemm_sampled(gpu):
+    _sampled_compare(workloads.C3, gpu, unfused=True)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3])
+def test_linear_unfused_prefill_c4_sampled(gpu, idx):
+    _sampled_compare(workloads.C4[idx], gpu, unfused=True)
+
+
+def test_linear_unfused_matches_fused_full(gpu):
+    """Both prefill paths produce the same accumulators and outputs on the
+    full M=2048, K=4096, N=14336 problem (the oracle checks samples of it)."""
+    lin = workloads.C3
+    C, alpha, packed = random_format([2070], lin.N, lin.K)
+    x = workloads.gaussian_matrix([2071], lin.M, lin.K)
+    _, _, acc_f, y_f = run_linear(x, C, alpha, packed, lin.N, gpu)
+    _, _, acc_u, y_u = run_linear(x, C, alpha, packed, lin.N, gpu, unfused=True)
+    np.testing.assert_array_equal(acc_u, acc_f)
+    np.testing.assert_array_equal(y_u, y_f)
+
+
+def test_linear_unfused_workspace_reuse(gpu):
+    """A workspace larger than needed, reused by a second, smaller call."""
+    K1, N1, K2, N2 = 1040, 97, 256, 48
+    ws = torch.empty((s3d8.unfused_workspace_bytes(N1, K1),), dtype=torch.int8, device=gpu)
+    for (M, K, N, seed) in [(33, K1, N1, 2080), (17, K2, N2, 2081)]:
+        C, alpha, packed = random_format([seed], N, K)
+        x = workloads.gaussian_matrix([seed + 100], M, K)
+        xq, xs = s3d8.quant_act(dev(x, gpu))
+        tiled = s3d8.tile(dev(packed, gpu), N)
+        y, acc = s3d8.linear_unfused(xq, xs, tiled, dev(C, gpu), dev(alpha.view(np.int16), gpu), N,
+                                     workspace=ws, return_acc=True)
+        torch.cuda.synchronize()
+        _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+        check_y(y.cpu().numpy(), y_r)

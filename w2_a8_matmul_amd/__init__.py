@@ -20,7 +20,8 @@ from ._lib import S3D8Error, call, lib  # noqa: F401
 
 __all__ = [
     "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "tiled_bytes", "pack", "encode",
-    "tile", "quant_act", "linear", "forward", "dequant", "PackedLinear",
+    "tile", "quant_act", "linear", "linear_unfused", "unfused_workspace_bytes", "forward", "dequant",
+    "PackedLinear",
 ]
 
 
@@ -163,6 +164,38 @@ def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_ac
         call("s3d8_linear", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(),
              centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
              acc.data_ptr() if acc is not None else None, _stream(xq))
+    if return_acc:
+        return y, acc
+    return y
+
+
+def unfused_workspace_bytes(N: int, K: int) -> int:
+    return int(lib().s3d8_unfused_workspace_bytes(N, K))
+
+
+def linear_unfused(xq, xs, tiled, centroids, scales, N: int, workspace=None, y=None, acc=None,
+                   return_acc: bool = False):
+    """Same result as ``linear``: the matrix is decoded once into an INT8
+    workspace (allocated here unless given), then an INT8 GEMM runs on it."""
+    torch = _torch()
+    _dev_check(xq, torch.int8, "xq")
+    _dev_check(xs, torch.float32, "xs")
+    scales = _scales_view(scales)
+    M, K = xq.shape
+    _check_weights(tiled, centroids, scales, N, K)
+    wbytes = unfused_workspace_bytes(N, K)
+    if workspace is None:
+        workspace = torch.empty((wbytes,), dtype=torch.int8, device=xq.device)
+    _dev_check(workspace, torch.int8, "workspace")
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    if return_acc and acc is None:
+        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    with torch.cuda.device(xq.device):
+        call("s3d8_linear_unfused", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(),
+             centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
+             acc.data_ptr() if acc is not None else None, workspace.data_ptr(), workspace.numel(),
+             _stream(xq))
     if return_acc:
         return y, acc
     return y

@@ -38,6 +38,8 @@ SIGNATURES = {
     "s3d8_linear": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "s3d8_forward": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
     "s3d8_dequant": (_I32, [_P, _P, _I64, _I64, _P, _P]),
+    "s3d8_unfused_workspace_bytes": (_I64, [_I64, _I64]),
+    "s3d8_linear_unfused": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
 }
 
 _lib = None

@@ -868,9 +868,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
 // three outputs go out as one 12-byte store, 384 contiguous bytes per row and
 // half wave.
 //
-// Workgroups are mapped XCD-aware: workgroup w runs on XCD w % 8, so each
-// XCD gets a contiguous range of tiles, weight column fastest, and the tiles
-// of one XCD share their activation rows through its L2.
+// Workgroups are mapped XCD-aware and in groups (gemm_tile), so that the
+// tiles resident on one XCD share activation and weight tiles in its L2.
 constexpr int kGemmBM = 128;      // token rows per workgroup
 constexpr int kGemmBF = 8;        // weight fragments (16 triples) per workgroup
 constexpr int kGemmRT = 4;        // 32-row tiles per wave
@@ -879,6 +878,26 @@ constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
 constexpr int kXcds = 8;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
+
+// Tile of workgroup blockIdx.x.  Workgroup w runs on XCD w % 8; each XCD
+// takes a contiguous range of tile indices, and tile indices run over
+// groups of kGroupM row blocks, row block fastest within a group and
+// column block next: the ~32 workgroups resident on one XCD then cover
+// about 8 row blocks x 4 column blocks, so their activation and weight
+// tiles are shared through that XCD's L2 instead of each workgroup
+// streaming its own weight stripe.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
+    const int nwg = nbm * nbn;
+    const int per_xcd = (nwg + kXcds - 1) / kXcds;
+    const int L = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (L >= nwg) return false;
+    const int group = L / (kGroupM * nbn), r = L - group * (kGroupM * nbn);
+    const int gm = min(kGroupM, nbm - group * kGroupM);
+    bm = group * kGroupM + r % gm;
+    bn = r / gm;
+    return true;
+}
 
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
@@ -897,11 +916,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     const int tiles16 = (T + 15) >> 4;
     const uint32_t lane_off = (uint32_t)lane << 2;
 
-    const int nwg = nbm * nbn;
-    const int per_xcd = (nwg + kXcds - 1) / kXcds;
-    const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (L >= nwg) return;  // padding workgroup (grid rounded up to a multiple of 8)
-    const int bm = L / nbn, bn = L - bm * nbn;
+    int bm, bn;
+    if (!gemm_tile(nbm, nbn, bm, bn)) return;  // padding workgroup (grid rounded up to a multiple of 8)
     const int row0 = bm * kGemmBM;
     const int frag0 = bn * kGemmBF + wave * 2;
 
@@ -1115,6 +1131,210 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
         for (int d = 0; d < 3; ++d) {
             const int64_t i = 3 * t + d;
             if (i < N) *reinterpret_cast<v4i *>(w + i * K + j) = o[d];
+        }
+    }
+}
+
+// --------------------------------------------------------------- unfused prefill
+
+// The pages' strategy for many token rows: decode the matrix once per call to
+// channel-INT8 in HBM, then run a plain INT8 GEMM.  Each weight byte is then
+// decoded once per call, instead of once per 128-row tile of the fused GEMM.
+
+// Tiled S3D8 -> channel-INT8 in the B-operand order of the INT8 GEMM: the
+// decoded matrix is cut into fragments of 32 channels x 64 input columns,
+// fragment (channel tile ct, block b) at byte (ct * KB + b) * 2048; inside
+// it, 16-byte unit (kh * 64 + c + 32 h) holds channel 32 ct + c at columns
+// 64 b + 32 kh + 16 h .. + 15 (the B operand of v_mfma_i32_32x32x32_i8 for
+// lane c + 32 h, k-half kh).  Channels past 3T and columns past K are not
+// written: they only meet zero activations or outputs that are never
+// stored.  Thread c handles 16-byte chunk c of the tiled matrix: fragment
+// c / 64, lane c % 64 = triple n + 16 g of the fragment, columns 16 g ..
+__global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
+    const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids, int K, int T, int KB,
+    int64_t nchunks, int8_t *__restrict__ w8) {
+    __shared__ uint32_t tab[kTabWords];
+    __shared__ uint32_t clw[24];
+    stage_and_build_table(tab, clw, centroids);
+    const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
+    for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
+         c += (int64_t)gridDim.x * kDequantThreads) {
+        const int64_t frag = c >> 6;
+        const int l = (int)(c & 63);
+        const int64_t tile = frag / KB;
+        const int blk = (int)(frag - tile * KB);
+        const int64_t t = tile * 16 + (l & 15);
+        const int g = l >> 4;
+        if (t >= T || blk * 64 + g * 16 >= K) continue;
+        const uint4 p = *reinterpret_cast<const uint4 *>(tiled + c * 16);
+        v4i o[3];
+        decode16(p, lane_off, tab, o[0], o[1], o[2]);
+        const int kh = g >> 1, h = g & 1;
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+            const int64_t ch = 3 * t + d;
+            const int64_t ct = ch >> 5;
+            const int cc = (int)(ch & 31);
+            *reinterpret_cast<v4i *>(w8 + (ct * KB + blk) * 2048 + kh * 1024 + (cc + 32 * h) * 16) = o[d];
+        }
+    }
+}
+
+// INT8 x INT8 GEMM on v_mfma_i32_32x32x32_i8: y = (xs * acc) * alpha.
+// Workgroup tile 128 token rows x 384 channels, 4 waves side by side along
+// N, wave tile 128 x 96 (4 x 3 accumulators of 32 x 32).  Per 64-column
+// block the activation tile (XOR-swizzled as in the fused GEMM) and the
+// weight fragments (already in B-operand lane order, 1 KiB contiguous per
+// load) are copied into a five-slot LDS ring four blocks ahead; the MFMAs
+// read both operands from LDS.
+constexpr int kI8Slots = 5;
+constexpr int kI8Ahead = kI8Slots - 1;
+
+__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                      int M, int K, int N, int NP, const int8_t *__restrict__ w8,
+                                                      const uint16_t *__restrict__ scales, float *__restrict__ y,
+                                                      int32_t *__restrict__ acc_out, int nbm, int nbn) {
+    __shared__ __attribute__((aligned(16))) int8_t abuf[kI8Slots][kGemmBM * 64];
+    __shared__ __attribute__((aligned(16))) int8_t bbuf[kI8Slots][4 * 6 * 1024];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c32 = lane & 31, h = lane >> 5;
+    const int KB = (K + 63) >> 6;
+
+    int bm, bn;
+    if (!gemm_tile(nbm, nbn, bm, bn)) return;
+    const int row0 = bm * kGemmBM;
+    const int ch0 = bn * 384 + wave * 96;  // first channel of this wave
+
+    const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
+    const v4i rw = rsrc_words(w8, (uint32_t)((NP + 31) / 32) * (uint32_t)KB * 2048u);
+
+    uint32_t aoff[2];
+    int acol[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int u = 64 * (2 * wave + j) + lane;
+        const int row = u >> 2;
+        const int chunk = (u & 3) ^ ((row >> 2) & 3);
+        aoff[j] = row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        acol[j] = 16 * chunk;
+    }
+    // B operand (column tile ct, k-half kh) of lane L: 16 bytes at unit
+    // kh * 64 + L of fragment (channel tile ch0 / 32 + ct, block kb)
+    uint32_t boff[3];
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct) {
+        const int ctile = ch0 / 32 + ct;
+        boff[ct] = 32 * ctile < NP ? (uint32_t)ctile * (uint32_t)KB * 2048u + 16u * lane : kOOB;
+    }
+    const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), bbase = S3D8_LDS_OFFSET(&bbuf[0][0]);
+    // eight loads per wave and block, also past the end (they read nothing)
+    auto issue = [&](int kb, int slot) {
+        const bool live = kb < KB;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            load_to_lds16(abase + (uint32_t)(kGemmBM * 64) * slot + 1024u * (2 * wave + j),
+                          (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bool ok = live && boff[ct] != kOOB;
+                load_to_lds16(bbase + (uint32_t)(4 * 6 * 1024) * slot + 6144u * wave + 1024u * (2 * ct + kh),
+                              ok ? boff[ct] + 2048u * kb + 1024u * kh : kOOB, rw);
+            }
+    };
+
+    const int swz = (c32 >> 2) & 3;
+    const int ard0 = c32 * 64 + 16 * (h ^ swz), ard1 = c32 * 64 + 16 * ((h ^ swz) ^ 2);
+
+#pragma unroll
+    for (int sl = 0; sl < kI8Ahead; ++sl) issue(sl, sl);
+
+    v16i acc[kGemmRT][3];
+#pragma unroll
+    for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) acc[i][d] = v16i{};
+
+    // operands of one block: A for 4 row tiles x 2 k-halves, B for 3 column
+    // tiles x 2 k-halves (14 x 16 bytes per lane)
+    struct Ops {
+        v4i a[kGemmRT][2], b[3][2];
+    };
+    auto read_ops = [&](Ops &o, int slot) {
+        const int8_t *ab = abuf[slot];
+        const int8_t *bb = bbuf[slot] + 6144 * wave + 16 * lane;
+#pragma unroll
+        for (int i = 0; i < kGemmRT; ++i) {
+            o.a[i][0] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard0);
+            o.a[i][1] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard1);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 3; ++ct)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) o.b[ct][kh] = *reinterpret_cast<const v4i *>(bb + 1024 * (2 * ct + kh));
+    };
+    auto mfmas = [&](const Ops &o) {
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+                for (int ct = 0; ct < 3; ++ct)
+                    acc[i][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[i][kh], o.b[ct][kh], acc[i][ct], 0, 0, 0);
+    };
+
+    // block kb (operands already in registers `cur`): wait until blocks <=
+    // kb + 1 are in LDS for every wave (16 loads = blocks kb + 2, kb + 3 may
+    // still fly), refill the slot of block kb - 1 with block kb + 4, read
+    // block kb + 1's operands into `nxt` while the MFMAs of block kb run
+    static_assert(kI8Ahead == 4, "the vmcnt immediates below assume four blocks in flight");
+    auto block = [&](const Ops &cur, Ops &nxt, int kb, int slot) {
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(kb + kI8Ahead, slot == 0 ? kI8Slots - 1 : slot - 1);
+        read_ops(nxt, slot == kI8Slots - 1 ? 0 : slot + 1);
+        mfmas(cur);
+    };
+
+    Ops o0, o1;
+    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // block 0 in LDS for every wave
+    read_ops(o0, 0);
+    int kb = 0, slot = 0;
+#pragma unroll 1
+    for (; kb + 1 < KB; kb += 2) {
+        block(o0, o1, kb, slot);
+        slot = slot == kI8Slots - 1 ? 0 : slot + 1;
+        block(o1, o0, kb + 1, slot);
+        slot = slot == kI8Slots - 1 ? 0 : slot + 1;
+    }
+    if (kb < KB) block(o0, o1, kb, slot);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    // epilogue: lane (c, h) holds column c of each column tile, rows
+    // 32 i + 8 (v / 4) + 4 h + v % 4
+    float sc[3];
+#pragma unroll
+    for (int ct = 0; ct < 3; ++ct) {
+        const int ch = ch0 + 32 * ct + c32;
+        sc[ct] = ch < N ? bf16_to_f32(scales[ch]) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < kGemmRT; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            if (row >= M) continue;
+            const float sx = xs[row];
+#pragma unroll
+            for (int ct = 0; ct < 3; ++ct) {
+                const int ch = ch0 + 32 * ct + c32;
+                if (ch < N) {
+                    y[(int64_t)row * N + ch] = (sx * (float)acc[i][ct][v]) * sc[ct];
+                    if (acc_out) acc_out[(int64_t)row * N + ch] = acc[i][ct][v];
+                }
+            }
         }
     }
 }
@@ -1342,6 +1562,42 @@ int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint
     rc = s3d8_quant_act(x, M, K, xq, xs, stream);
     if (rc) return rc;
     return s3d8_linear(xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, stream);
+}
+
+int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
+    if (N <= 0 || K <= 0) return -1;
+    return (3 * ((N + 2) / 3) + 31) / 32 * ((K + 63) / 64) * 2048;
+}
+
+int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16, float *y,
+                            int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
+    if (!xq || !xs || !workspace) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    if (rc) return rc;
+    if (!aligned16(xq) || !aligned16(workspace))
+        return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
+    const int64_t T = (N + 2) / 3;
+    const int64_t wbytes = s3d8_unfused_workspace_bytes(N, K);
+    if (wbytes > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "decoded matrix over 2^31 bytes");
+    if (workspace_bytes < wbytes) return s3d8::fail(S3D8_ERR_INVALID_ARG, "workspace smaller than s3d8_unfused_workspace_bytes");
+    int cus = 0;
+    rc = check_device(&cus);
+    if (rc) return rc;
+    const int KB = (int)((K + 63) / 64);
+    const int64_t nchunks = tiled_bytes(N, K) / 16;
+    int64_t blocks = (nchunks + kDequantThreads - 1) / kDequantThreads;
+    if (blocks > (int64_t)cus * 2) blocks = (int64_t)cus * 2;
+    hipLaunchKernelGGL(dequant_tiled_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0, (hipStream_t)stream,
+                       tiled, reinterpret_cast<const uint32_t *>(centroids), (int)K, (int)T, KB, nchunks, workspace);
+    const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
+    const int nbn = (int)((3 * T + 383) / 384);
+    const int64_t nwg = (int64_t)nbm * nbn;
+    const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
+    if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
+    hipLaunchKernelGGL(gemm_i8_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K,
+                       (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
+    return launch_status();
 }
 
 int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K, int8_t *w,
