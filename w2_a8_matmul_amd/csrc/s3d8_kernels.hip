@@ -876,6 +876,8 @@ constexpr int kGemmRT = 4;        // 32-row tiles per wave
 constexpr int kGemmSlots = 5;     // LDS ring slots
 constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
 constexpr int kXcds = 8;
+// 128 rows of fp32 output stay under 2^31 bytes (32-bit store offsets)
+constexpr int64_t kGemmMaxN = (int64_t(1) << 31) / (4 * kGemmBM) - 1;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 
@@ -899,6 +901,94 @@ __device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
     return true;
 }
 
+__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Epilogue of a wave's 128-row block: y[row][col_j] = (xs[row] * acc) *
+// sc[j] for the three 32 x 32 accumulator columns j of each row tile i
+// (and, kAcc, the accumulators themselves into acc_out).  Lane (c, h) holds
+// rows 32 i + 8 (v / 4) + 4 h + v % 4 of accumulator register v; coff[j] is
+// the byte offset of its column j within a row of y (kOOB for a column past
+// N) and sc[j] that column's channel scale.
+//
+// Branch-free: the lane's 16 token scales arrive as four 16-byte buffer
+// loads per row tile (rows past M read as zero), and every store is a
+// buffer store whose offset has bit 31 set (out of range: dropped) for a row
+// past M or a column past N.  kTriple: the three columns are channels 3t,
+// 3t + 1, 3t + 2 of one triple and go out as one 12-byte store; a lane whose
+// triple straddles N (at most one per matrix) stores its valid channels one
+// by one instead, in a second pass only its wave runs.  Offsets stay below
+// 2^32: the caller keeps 128 rows of y under 2^31 bytes.
+template <bool kTriple, bool kAcc>
+__device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], const float *__restrict__ xs, int M,
+                                                int N, int row0, int h, const float (&sc)[3], const uint32_t (&coff)[3],
+                                                float *__restrict__ y, int32_t *__restrict__ acc_out) {
+    const int nrows = min(M - row0, kGemmBM);
+    const uint32_t rowb = 4u * (uint32_t)N;
+    const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
+    float4 sx[kGemmRT][4];
+#pragma unroll
+    for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            sx[i][g] = __builtin_bit_cast(float4, bload16(rxs, 4u * (uint32_t)(32 * i + 8 * g + 4 * h)));
+    const auto ry = make_rsrc(y + (int64_t)row0 * N, rowb * (uint32_t)nrows);
+    const auto ra = make_rsrc(acc_out + (int64_t)row0 * N, kAcc ? rowb * (uint32_t)nrows : 0u);
+    uint32_t base[3];
+#pragma unroll
+    for (int j = 0; j < 3; ++j) base[j] = coff[j] + (uint32_t)(4 * h) * rowb;
+    // bit 31 when row 32 i + 8 (v / 4) + v % 4 + 4 h is past M
+    auto dead = [&](int r) { return (uint32_t)(nrows - 1 - r - 4 * h) & kOOB; };
+    auto out = [&](int i, int v, int j) {
+        return __float_as_uint((sx[i][v >> 2][v & 3] * (float)acc[i][j][v]) * sc[j]);
+    };
+    if constexpr (kTriple) {
+        typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+        const bool split = coff[0] != kOOB && coff[2] == kOOB;
+        const uint32_t base3 = split ? kOOB : base[0];
+#pragma unroll
+        for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + (v & 3);
+                const uint32_t off = (base3 + (uint32_t)r * rowb) | dead(r);
+                __builtin_amdgcn_raw_buffer_store_b96(u3{out(i, v, 0), out(i, v, 1), out(i, v, 2)}, ry, off, 0, 0);
+                if constexpr (kAcc)
+                    __builtin_amdgcn_raw_buffer_store_b96(
+                        u3{(uint32_t)acc[i][0][v], (uint32_t)acc[i][1][v], (uint32_t)acc[i][2][v]}, ra, off, 0, 0);
+            }
+        if (__builtin_amdgcn_ballot_w64(split) == 0) return;
+#pragma unroll
+        for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + (v & 3);
+                const uint32_t d = dead(r) | (split ? 0u : kOOB);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint32_t off = (base[j] + (uint32_t)r * rowb) | d;
+                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, 0);
+                    if constexpr (kAcc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra, off, 0, 0);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kGemmRT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const uint32_t off = (base[j] + (uint32_t)r * rowb) | dead(r);
+                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, 0);
+                    if constexpr (kAcc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra, off, 0, 0);
+                }
+            }
+    }
+}
+
+template <bool kAcc>
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
                                                    const uint32_t *__restrict__ centroids,
@@ -1071,39 +1161,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // loads of blocks past the end are still in flight: drain before exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // epilogue: y = (xs[row] * acc) * alpha[ch], channel 3 (16 frag0 + c) + d
+    // epilogue: y = (xs[row] * acc) * alpha[ch] for channels 3 (16 frag0 +
+    // c) + d, the three contiguous channels of lane c's triple
     const int ch0 = 3 * (16 * frag0 + c32);
     float sc[3];
+    uint32_t coff[3];
+    const auto rsc = make_rsrc(scales, (uint32_t)N * 2u);
 #pragma unroll
-    for (int d = 0; d < 3; ++d) sc[d] = ch0 + d < N ? bf16_to_f32(scales[ch0 + d]) : 0.0f;
-    const bool full = ch0 + 2 < N;
-    typedef float f3u __attribute__((ext_vector_type(3))) __attribute__((aligned(4)));
-#pragma unroll
-    for (int i = 0; i < kGemmRT; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (row >= M) continue;
-            const float sx = xs[row];
-            float o[3];
-#pragma unroll
-            for (int d = 0; d < 3; ++d) o[d] = (sx * (float)acc[i][d][v]) * sc[d];
-            float *dst = y + (int64_t)row * N + ch0;
-            if (full) {
-                *reinterpret_cast<f3u *>(dst) = f3u{o[0], o[1], o[2]};
-            } else {
-#pragma unroll
-                for (int d = 0; d < 3; ++d)
-                    if (ch0 + d < N) dst[d] = o[d];
-            }
-            if (acc_out) {
-                int32_t *da = acc_out + (int64_t)row * N + ch0;
-#pragma unroll
-                for (int d = 0; d < 3; ++d)
-                    if (ch0 + d < N) da[d] = acc[i][d][v];
-            }
-        }
+    for (int d = 0; d < 3; ++d) {
+        const bool ok = ch0 + d < N;
+        coff[d] = ok ? 4u * (uint32_t)(ch0 + d) : kOOB;
+        sc[d] = bf16_to_f32(bload2(rsc, ok ? 2u * (uint32_t)(ch0 + d) : kOOB));
     }
+    store_tile_rows<true, kAcc>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- dequant
@@ -1190,6 +1260,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
 constexpr int kI8Slots = 5;
 constexpr int kI8Ahead = kI8Slots - 1;
 
+template <bool kAcc>
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       int M, int K, int N, int NP, const int8_t *__restrict__ w8,
                                                       const uint16_t *__restrict__ scales, float *__restrict__ y,
@@ -1312,31 +1383,18 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     if (kb < KB) block(o0, o1, kb, slot);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-    // epilogue: lane (c, h) holds column c of each column tile, rows
-    // 32 i + 8 (v / 4) + 4 h + v % 4
+    // epilogue: lane (c, h) holds column c of each column tile for rows
+    // 32 i + 8 (v / 4) + 4 h + v % 4 (store_tile_rows)
     float sc[3];
+    uint32_t coff[3];
+    const auto rsc = make_rsrc(scales, (uint32_t)N * 2u);
 #pragma unroll
     for (int ct = 0; ct < 3; ++ct) {
         const int ch = ch0 + 32 * ct + c32;
-        sc[ct] = ch < N ? bf16_to_f32(scales[ch]) : 0.0f;
+        coff[ct] = ch < N ? 4u * (uint32_t)ch : kOOB;
+        sc[ct] = bf16_to_f32(bload2(rsc, ch < N ? 2u * (uint32_t)ch : kOOB));
     }
-#pragma unroll
-    for (int i = 0; i < kGemmRT; ++i) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = row0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-            if (row >= M) continue;
-            const float sx = xs[row];
-#pragma unroll
-            for (int ct = 0; ct < 3; ++ct) {
-                const int ch = ch0 + 32 * ct + c32;
-                if (ch < N) {
-                    y[(int64_t)row * N + ch] = (sx * (float)acc[i][ct][v]) * sc[ct];
-                    if (acc_out) acc_out[(int64_t)row * N + ch] = acc[i][ct][v];
-                }
-            }
-        }
-    }
+    store_tile_rows<false, kAcc>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- host glue
@@ -1517,13 +1575,14 @@ int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int
     rc = check_device(&cus);
     if (rc) return rc;
     if (M > 16) {
+        if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 4194303 is not supported for M > 16");
         const int64_t T = (N + 2) / 3;
         const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
         const int nbn = (int)(((T + 15) / 16 + kGemmBF - 1) / kGemmBF);
         const int64_t nwg = (int64_t)nbm * nbn;
         const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
         if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-        hipLaunchKernelGGL(gemm_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M,
+        hipLaunchKernelGGL(acc_out ? gemm_kernel<true> : gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M,
                            (int)K, (int)N, (int)T, tiled, reinterpret_cast<const uint32_t *>(centroids),
                            scales_bf16, y, acc_out, nbm, nbn);
         return launch_status();
@@ -1577,6 +1636,7 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
     if (rc) return rc;
     if (!aligned16(xq) || !aligned16(workspace))
         return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
+    if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 4194303 is not supported");
     const int64_t T = (N + 2) / 3;
     const int64_t wbytes = s3d8_unfused_workspace_bytes(N, K);
     if (wbytes > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "decoded matrix over 2^31 bytes");
@@ -1595,7 +1655,7 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
     const int64_t nwg = (int64_t)nbm * nbn;
     const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
     if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-    hipLaunchKernelGGL(gemm_i8_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K,
+    hipLaunchKernelGGL(acc_out ? gemm_i8_kernel<true> : gemm_i8_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K,
                        (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
     return launch_status();
 }
