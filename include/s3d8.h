@@ -174,7 +174,7 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
  *   y            out, device fp32 [M][N], row-major.
  *   acc_out      optional out (NULL to skip), device int32 [M][N]: the
  *                accumulators before the epilogue, for verification.
- * Errors: INVALID_ARG, SHAPE (also N > 4194303 when M > 16), ALIGN, DEVICE,
+ * Errors: INVALID_ARG, SHAPE (also N > 3355442 when M > 16), ALIGN, DEVICE,
  * HIP. */
 int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
                     const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
@@ -215,7 +215,7 @@ int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K);
  *                need separate workspaces.
  *   workspace_bytes  its size.
  * Errors: INVALID_ARG (also a workspace too small), SHAPE (decoded matrix
- * over 2^31 bytes, or N > 4194303), ALIGN, DEVICE, HIP. */
+ * over 2^31 bytes, or N > 3355442), ALIGN, DEVICE, HIP. */
 int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
                             const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
                             float *y, int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes,

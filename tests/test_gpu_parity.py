@@ -252,6 +252,21 @@ def test_linear_prefill_c4_sampled(gpu, idx):
     _sampled_compare(workloads.C4[idx], gpu)
 
 
+def test_linear_prefill_five_row_tiles(gpu):
+    """A shape whose workgroup count makes the GEMM take 160-row tiles (5 row
+    tiles per wave) on a 256-CU device: 8 row blocks instead of 10, 256
+    workgroups in one round instead of 320 in two.  Ragged in every
+    dimension (last row block 150 rows, K = 64 + 16, a partial last triple
+    tile), compared in full."""
+    M, K, N = 1270, 80, 12280
+    C, alpha, packed = random_format([2090, M, K, N], N, K)
+    x = workloads.gaussian_matrix([2091, M, K], M, K)
+    xq, xs, acc, y = run_linear(x, C, alpha, packed, N, gpu)
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
 def test_linear_repeated_calls_are_identical(gpu):
     lin = workloads.C0
     C, alpha, packed = packed_matrix(lin)

@@ -876,8 +876,9 @@ constexpr int kGemmRT = 4;        // 32-row tiles per wave
 constexpr int kGemmSlots = 5;     // LDS ring slots
 constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
 constexpr int kXcds = 8;
-// 128 rows of fp32 output stay under 2^31 bytes (32-bit store offsets)
-constexpr int64_t kGemmMaxN = (int64_t(1) << 31) / (4 * kGemmBM) - 1;
+// a workgroup's rows of fp32 output stay under 2^31 bytes (32-bit store offsets)
+constexpr int kGemmMaxRT = 5;     // most 32-row tiles per wave of any GEMM variant
+constexpr int64_t kGemmMaxN = (int64_t(1) << 31) / (4 * 32 * kGemmMaxRT) - 1;
 
 typedef int32_t v16i __attribute__((ext_vector_type(16)));
 
@@ -901,11 +902,28 @@ __device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
     return true;
 }
 
+// s_waitcnt vmcnt(N) for the loads the compiler does not see (LDS-DMA), and
+// the same followed by lgkmcnt(0) and a workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N == 8 || N == 10 || N == 12 || N == 15, "add the immediate");
+    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    if constexpr (N == 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    static_assert(N == 8 || N == 10, "add the immediate");
+    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
-// Epilogue of a wave's 128-row block: y[row][col_j] = (xs[row] * acc) *
+// Epilogue of a wave's block of 32 RT rows: y[row][col_j] = (xs[row] * acc) *
 // sc[j] for the three 32 x 32 accumulator columns j of each row tile i
 // (and, kAcc, the accumulators themselves into acc_out).  Lane (c, h) holds
 // rows 32 i + 8 (v / 4) + 4 h + v % 4 of accumulator register v; coff[j] is
@@ -920,16 +938,16 @@ __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
 // triple straddles N (at most one per matrix) stores its valid channels one
 // by one instead, in a second pass only its wave runs.  Offsets stay below
 // 2^32: the caller keeps 128 rows of y under 2^31 bytes.
-template <bool kTriple, bool kAcc>
-__device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], const float *__restrict__ xs, int M,
+template <bool kTriple, bool kAcc, int RT>
+__device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const float *__restrict__ xs, int M,
                                                 int N, int row0, int h, const float (&sc)[3], const uint32_t (&coff)[3],
                                                 float *__restrict__ y, int32_t *__restrict__ acc_out) {
-    const int nrows = min(M - row0, kGemmBM);
+    const int nrows = min(M - row0, 32 * RT);
     const uint32_t rowb = 4u * (uint32_t)N;
     const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
-    float4 sx[kGemmRT][4];
+    float4 sx[RT][4];
 #pragma unroll
-    for (int i = 0; i < kGemmRT; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             sx[i][g] = __builtin_bit_cast(float4, bload16(rxs, 4u * (uint32_t)(32 * i + 8 * g + 4 * h)));
@@ -948,7 +966,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], c
         const bool split = coff[0] != kOOB && coff[2] == kOOB;
         const uint32_t base3 = split ? kOOB : base[0];
 #pragma unroll
-        for (int i = 0; i < kGemmRT; ++i)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = 32 * i + 8 * (v >> 2) + (v & 3);
@@ -960,7 +978,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], c
             }
         if (__builtin_amdgcn_ballot_w64(split) == 0) return;
 #pragma unroll
-        for (int i = 0; i < kGemmRT; ++i)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = 32 * i + 8 * (v >> 2) + (v & 3);
@@ -974,7 +992,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], c
             }
     } else {
 #pragma unroll
-        for (int i = 0; i < kGemmRT; ++i)
+        for (int i = 0; i < RT; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int r = 32 * i + 8 * (v >> 2) + (v & 3);
@@ -988,14 +1006,18 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[kGemmRT][3], c
     }
 }
 
-template <bool kAcc>
+template <int RT, bool kAcc>
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
                                                    const uint32_t *__restrict__ centroids,
                                                    const uint16_t *__restrict__ scales, float *__restrict__ y,
                                                    int32_t *__restrict__ acc_out, int nbm, int nbn) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
-    __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][kGemmBM * 64];
+    constexpr int BM = 32 * RT;          // token rows per workgroup
+    constexpr int NA = (2 * RT + 3) / 4;  // activation loads per wave and block
+    constexpr int ND = NA + 2;            // all loads per wave and block
+    __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][BM * 64];
+    __shared__ __attribute__((aligned(16))) int8_t spill[(4 * NA > 2 * RT) ? 1024 : 16];
     __shared__ __attribute__((aligned(16))) int8_t wbuf[kGemmSlots][kGemmBF * 1024];
     __shared__ uint32_t clw[24];
 
@@ -1008,7 +1030,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 
     int bm, bn;
     if (!gemm_tile(nbm, nbn, bm, bn)) return;  // padding workgroup (grid rounded up to a multiple of 8)
-    const int row0 = bm * kGemmBM;
+    const int row0 = bm * BM;
     const int frag0 = bn * kGemmBF + wave * 2;
 
     uint32_t cw[24];
@@ -1018,16 +1040,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
     const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
 
-    // activation copy: wave w moves 16-byte units u = 64 (2 w + j) + lane of
-    // the 128 x 64 tile; unit u holds row u / 4, chunk (u % 4) ^ ((row / 4) % 4)
-    uint32_t aoff[2];
-    int acol[2];
+    // activation copy: wave w moves 16-byte units u = 64 (NA w + j) + lane of
+    // the BM x 64 tile; unit u holds row u / 4, chunk (u % 4) ^ ((row / 4) % 4).
+    // Loads past the tile (when 4 NA > 2 RT) read nothing into `spill`.
+    uint32_t aoff[NA];
+    int acol[NA];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int u = 64 * (2 * wave + j) + lane;
+    for (int j = 0; j < NA; ++j) {
+        const int u = 64 * (NA * wave + j) + lane;
         const int row = u >> 2;
         const int chunk = (u & 3) ^ ((row >> 2) & 3);
-        aoff[j] = row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        aoff[j] = row < BM && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
         acol[j] = 16 * chunk;
     }
     // weight copy: lane (c, h), k-half kh takes triple c of the wave at
@@ -1040,13 +1063,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
                                  : kOOB;
 
     const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), wbase = S3D8_LDS_OFFSET(&wbuf[0][0]);
-    // four loads per wave and block, also for blocks past the end (they
-    // read nothing), so that every wait below counts the same
+    const uint32_t sbase = S3D8_LDS_OFFSET(&spill[0]);
+    // ND loads per wave and block, also for blocks past the end (they read
+    // nothing), so that every wait below counts the same
     auto issue = [&](int kb, int slot) {
         const bool live = kb < KB;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            load_to_lds16(abase + (uint32_t)(kGemmBM * 64) * slot + 1024u * (2 * wave + j),
+        for (int j = 0; j < NA; ++j)
+            load_to_lds16(NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j) : sbase,
                           (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
@@ -1058,22 +1082,24 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     const int swz = (c32 >> 2) & 3;
     const int ard0 = c32 * 64 + 16 * (h ^ swz), ard1 = c32 * 64 + 16 * ((h ^ swz) ^ 2);
 
-    // decode dword c of k-half kh of the raw weights into operand set bs
-    auto decode_piece = [&](const uint4 (&ps)[2], v4i (&bs)[2][3], int kh, int c) {
+    // decode of packed dword p (k-half p / 4, dword p % 4) of the raw
+    // weights, in two halves that the block below schedules apart: the four
+    // table lookups, and the 4 x 3 byte transpose into operand set bs
+    auto lookups = [&](const uint4 (&ps)[2], int p, uint32_t (&q)[4]) {
         const char *tb = reinterpret_cast<const char *>(tab);
+        const int kh = p >> 2, c = p & 3;
         const uint32_t dw = c == 0 ? ps[kh].x : c == 1 ? ps[kh].y : c == 2 ? ps[kh].z : ps[kh].w;
-        const uint32_t a0 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0400u);
-        const uint32_t a1 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0500u);
-        const uint32_t a2 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0600u);
-        const uint32_t a3 = __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0700u);
-        const uint32_t q0 = *reinterpret_cast<const uint32_t *>(tb + a0);
-        const uint32_t q1 = *reinterpret_cast<const uint32_t *>(tb + a1);
-        const uint32_t q2 = *reinterpret_cast<const uint32_t *>(tb + a2);
-        const uint32_t q3 = *reinterpret_cast<const uint32_t *>(tb + a3);
-        const uint32_t p01 = __builtin_amdgcn_perm(q1, q0, 0x05010400u);
-        const uint32_t p23 = __builtin_amdgcn_perm(q3, q2, 0x05010400u);
-        const uint32_t s01 = __builtin_amdgcn_perm(q1, q0, 0x0C0C0602u);
-        const uint32_t s23 = __builtin_amdgcn_perm(q3, q2, 0x0C0C0602u);
+        q[0] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0400u));
+        q[1] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0500u));
+        q[2] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0600u));
+        q[3] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0700u));
+    };
+    auto transpose = [&](const uint32_t (&q)[4], v4i (&bs)[2][3], int p) {
+        const int kh = p >> 2, c = p & 3;
+        const uint32_t p01 = __builtin_amdgcn_perm(q[1], q[0], 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(q[3], q[2], 0x05010400u);
+        const uint32_t s01 = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0602u);
+        const uint32_t s23 = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0602u);
         bs[kh][0][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x05040100u);
         bs[kh][1][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x07060302u);
         bs[kh][2][c] = (int32_t)__builtin_amdgcn_perm(s23, s01, 0x05040100u);
@@ -1100,64 +1126,94 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
             reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
         }
     }
-    static_assert(kGemmAhead == 4, "the vmcnt immediates below assume four blocks in flight");
-    asm volatile("s_waitcnt vmcnt(12)" ::: "memory");  // this wave's block 0 is in LDS
+    static_assert(kGemmAhead == 4, "the waits below assume four blocks in flight");
+    wait_vmcnt<3 * ND>();  // this wave's block 0 is in LDS
     __syncthreads();                                    // everyone's block 0, and the table
 
-    v16i acc[kGemmRT][3];
+    v16i acc[RT][3];
 #pragma unroll
-    for (int i = 0; i < kGemmRT; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int d = 0; d < 3; ++d) acc[i][d] = v16i{};
 
+    // operands of block 0 (A from LDS, B decoded)
+    auto read_a = [&](v4i (&a)[RT][2], int slot, int i) {
+        const int8_t *ab = abuf[slot];
+        a[i][0] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard0);
+        a[i][1] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard1);
+    };
+    v4i a0[RT][2], a1[RT][2];
     v4i b0[2][3], b1[2][3];
     {
         uint4 w0[2];
         read_w(w0, 0);
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int i = 0; i < RT; ++i) read_a(a0, 0, i);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) decode_piece(w0, b0, kh, c);
+        for (int p = 0; p < 8; ++p) {
+            uint32_t q[4];
+            lookups(w0, p, q);
+            transpose(q, b0, p);
+        }
     }
 
     // block kb (LDS slot `slot`): wait until blocks <= kb + 1 are in LDS for
-    // every wave (8 loads = blocks kb + 2, kb + 3 may stay in flight), refill
-    // the slot of block kb - 1 with block kb + 4, then MFMAs of A(kb) x bc
-    // with the decode of W(kb + 1) into bnx between them
-    auto block = [&](const v4i (&bc)[2][3], v4i (&bnx)[2][3], int kb, int slot) {
-        asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // every wave (2 ND loads = blocks kb + 2, kb + 3 may stay in flight),
+    // refill the slot of block kb - 1 with block kb + 4, then the 6 RT MFMAs
+    // of A(kb) x B(kb) in 2 RT groups of three, with the operands of block
+    // kb + 1 prepared between them.  Group g carries: the raw weights (g = 0),
+    // A row tile i (g = i % 4), the lookups of dwords 2 (g - 1) and 2 (g - 1)
+    // + 1, and the transposes of dwords 2 (g - 3) and 2 (g - 3) + 1, so that
+    // every LDS read has two groups of MFMAs to land behind.  Inside a group
+    // each MFMA is followed by a share of the VALU and LDS work, since one
+    // wave per SIMD only overlaps what lies between its MFMAs; sched_barrier
+    // keeps the compiler from regrouping across groups.
+    static_assert(2 * RT >= 7, "the block schedule needs seven groups");
+    auto block = [&](const v4i (&ac)[RT][2], v4i (&an)[RT][2], const v4i (&bc)[2][3], v4i (&bnx)[2][3], int kb,
+                     int slot) {
+        wait_vmcnt_barrier<2 * ND>();
         const int next = slot == kGemmSlots - 1 ? 0 : slot + 1;
         const int prev = slot == 0 ? kGemmSlots - 1 : slot - 1;
         issue(kb + kGemmAhead, prev);
-        const int8_t *ab = abuf[slot];
-        v4i a[kGemmRT][2];
-#pragma unroll
-        for (int i = 0; i < kGemmRT; ++i) {
-            a[i][0] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard0);
-            a[i][1] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard1);
-        }
         uint4 wn[2];
-        read_w(wn, next);
+        uint32_t q[8][4];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int g = 0; g < 2 * RT; ++g) {
+            const int kh = g / RT, i = g % RT;
 #pragma unroll
-            for (int i = 0; i < kGemmRT; ++i) {
+            for (int d = 0; d < 3; ++d)
+                acc[i][d] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i][kh], bc[kh][d], acc[i][d], 0, 0, 0);
+            if (g == 0) read_w(wn, next);
 #pragma unroll
-                for (int d = 0; d < 3; ++d)
-                    acc[i][d] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i][kh], bc[kh][d], acc[i][d], 0, 0, 0);
-                decode_piece(wn, bnx, kh, i);
+            for (int r = 0; r < RT; ++r)
+                if (g == r % 4) read_a(an, next, r);
+            if (g >= 1 && g <= 4) {
+                lookups(wn, 2 * (g - 1), q[2 * (g - 1)]);
+                lookups(wn, 2 * (g - 1) + 1, q[2 * (g - 1) + 1]);
             }
+            if (g >= 3 && g <= 6) {
+                transpose(q[2 * (g - 3)], bnx, 2 * (g - 3));
+                transpose(q[2 * (g - 3) + 1], bnx, 2 * (g - 3) + 1);
+            }
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // up to six VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // up to four LDS reads
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
     };
 
     int kb = 0, slot = 0;
 #pragma unroll 1
     for (; kb + 1 < KB; kb += 2) {
-        block(b0, b1, kb, slot);
+        block(a0, a1, b0, b1, kb, slot);
         slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
-        block(b1, b0, kb + 1, slot);
+        block(a1, a0, b1, b0, kb + 1, slot);
         slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
     }
-    if (kb < KB) block(b0, b1, kb, slot);
+    if (kb < KB) block(a0, a1, b0, b1, kb, slot);
     // loads of blocks past the end are still in flight: drain before exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
@@ -1367,6 +1423,14 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         issue(kb + kI8Ahead, slot == 0 ? kI8Slots - 1 : slot - 1);
         read_ops(nxt, slot == kI8Slots - 1 ? 0 : slot + 1);
         mfmas(cur);
+        // interleave the 14 operand reads of the next block with the first
+        // MFMAs of this one, so that their LDS latency hides behind them
+#pragma unroll
+        for (int q = 0; q < 14; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
     };
 
     Ops o0, o1;
@@ -1575,16 +1639,25 @@ int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int
     rc = check_device(&cus);
     if (rc) return rc;
     if (M > 16) {
-        if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 4194303 is not supported for M > 16");
+        if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
         const int64_t T = (N + 2) / 3;
-        const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
         const int nbn = (int)(((T + 15) / 16 + kGemmBF - 1) / kGemmBF);
+        // 4 or 5 row tiles per wave: the one that needs fewer workgroup
+        // rounds (one workgroup per CU), counted in units of row-tile work
+        auto cost = [&](int rt) {
+            const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
+            return (tiles + cus - 1) / cus * rt;
+        };
+        const int rt = cost(5) < cost(4) ? 5 : 4;
+        const int nbm = (int)((M + 32 * rt - 1) / (32 * rt));
         const int64_t nwg = (int64_t)nbm * nbn;
         const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
         if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-        hipLaunchKernelGGL(acc_out ? gemm_kernel<true> : gemm_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M,
-                           (int)K, (int)N, (int)T, tiled, reinterpret_cast<const uint32_t *>(centroids),
-                           scales_bf16, y, acc_out, nbm, nbn);
+        auto kern = rt == 5 ? (acc_out ? gemm_kernel<5, true> : gemm_kernel<5, false>)
+                            : (acc_out ? gemm_kernel<4, true> : gemm_kernel<4, false>);
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K, (int)N,
+                           (int)T, tiled, reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y, acc_out, nbm,
+                           nbn);
         return launch_status();
     }
     // the GEMV takes up to 16 token rows per launch
@@ -1636,7 +1709,7 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
     if (rc) return rc;
     if (!aligned16(xq) || !aligned16(workspace))
         return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
-    if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 4194303 is not supported");
+    if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported");
     const int64_t T = (N + 2) / 3;
     const int64_t wbytes = s3d8_unfused_workspace_bytes(N, K);
     if (wbytes > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "decoded matrix over 2^31 bytes");
