@@ -67,11 +67,11 @@ def measured_traffic(name, launches_bytes):
 
 
 def graph_launch_us(torch, fns, reps):
-    """Average duration of one launch: the launches fns[0..n-1] (one kernel
-    each) are captured back to back in one HIP graph, replayed `reps` times
-    between two events on the launching stream; the interval over n * reps
-    launches includes no host time, only the kernels and the gaps between
-    consecutive dispatches."""
+    """Average duration of one call: the calls fns[0..n-1] are captured back
+    to back in one HIP graph, replayed `reps` times between two events on
+    the launching stream; the interval over n * reps calls includes no host
+    time, only the kernels and the gaps between consecutive dispatches.  For
+    calls of one kernel launch each this is the kernel's average duration."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for f in fns:
@@ -215,15 +215,29 @@ def main():
             torch, [lambda r=r: s3d8.linear(xqp, xsp, dPp[r], dCp, dSp, lp.N, y=yp) for r in range(Rp)], 5)
         ops = 2.0 * lp.M * lp.K * lp.N
         tops = ops / (g_mean_us * 1e-6) / 1e12
-        log(f"prefill GEMM {lp.name}: {g_mean_us:.1f} us -> {tops:.1f} TOPS")
+        log(f"prefill GEMM {lp.name}: fused {g_mean_us:.1f} us -> {tops:.1f} TOPS")
+        # the pages' strategy for many rows: decode once to INT8, then an
+        # INT8 GEMM (two launches per call)
+        ws = torch.empty((s3d8.unfused_workspace_bytes(lp.N, lp.K),), dtype=torch.int8, device=dev)
+        s3d8.linear_unfused(xqp, xsp, dPp[0], dCp, dSp, lp.N, workspace=ws, y=yp)
+        torch.cuda.synchronize()
+        u_mean_us = graph_launch_us(
+            torch, [lambda r=r: s3d8.linear_unfused(xqp, xsp, dPp[r], dCp, dSp, lp.N, workspace=ws, y=yp)
+                    for r in range(Rp)], 5)
+        u_tops = ops / (u_mean_us * 1e-6) / 1e12
+        log(f"prefill GEMM {lp.name}: unfused (dequant + INT8 GEMM) {u_mean_us:.1f} us -> {u_tops:.1f} TOPS")
         prefill = {
             "workload": f"{lp.name}: M={lp.M} K={lp.K} N={lp.N}",
             "value": round(tops, 2), "unit": "INT8 TOPS", "us_per_launch": round(g_mean_us, 2),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
-                         "traffic": measured_traffic("gemm_c3", None)},
+                         "traffic": measured_traffic("gemm_c3", None),
+                         "kernel": "gemm_kernel (fused decode + INT8 MFMA, via s3d8_linear)"},
+            "unfused": {"value": round(u_tops, 2), "unit": "INT8 TOPS", "us_per_call": round(u_mean_us, 2),
+                        "frac": round(u_tops / INT8_PEAK_TOPS, 4),
+                        "kernels": "dequant_tiled_kernel + gemm_i8_kernel (s3d8_linear_unfused)"},
         }
-        del dPp
+        del dPp, ws
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -271,7 +285,7 @@ def main():
                    "weight_copies": R, "graph_steps": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel (fused, via s3d8_forward)", "kernel_us": round(lin_mean_us, 3),
+                     "kernel": "gemv_stream_kernel (fused quantise + decode GEMV, via s3d8_forward)", "kernel_us": round(lin_mean_us, 3),
                      "algorithmic_bytes": kernel_bytes},
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,

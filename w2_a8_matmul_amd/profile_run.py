@@ -8,7 +8,9 @@ Runs, in one process and in this order:
      N=14336, 28 distinct weight copies (so that every launch reads its
      weights from HBM, not from the Infinity Cache), 2 passes over them;
   3. ``gemm_c3``: s3d8_linear on the prefill shape M=2048, K=4096, N=14336,
-     4 launches.
+     4 launches;
+  4. the same problem through s3d8_linear_unfused (dequant_tiled_kernel +
+     gemm_i8_kernel), 4 calls.
 Weights are random S3D8 formats (uniform bytes, random table and scales):
 the bytes moved do not depend on the values.
 
@@ -79,6 +81,13 @@ def main() -> None:
         s3d8.linear(xq, xs, tiled, C, S, N, y=y)
     torch.cuda.synchronize()
     say(f"gemm_c3: 4 launches of s3d8_linear M={M} K={K} N={N}")
+
+    # 4. the unfused prefill path on the same problem
+    ws = torch.empty((s3d8.unfused_workspace_bytes(N, K),), dtype=torch.int8, device=dev)
+    for _ in range(4):
+        s3d8.linear_unfused(xq, xs, tiled, C, S, N, workspace=ws, y=y)
+    torch.cuda.synchronize()
+    say(f"gemm_c3 unfused: 4 calls of s3d8_linear_unfused M={M} K={K} N={N}")
 
 
 if __name__ == "__main__":
