@@ -571,10 +571,17 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Arguments used before the first loads come first, so that they are among
 // the kernel arguments preloaded into SGPRs.
+//
+// One instantiation per row count MR: the prologue runs once per launch from
+// a cold instruction cache, so its length in bytes is on the critical path;
+// with the row count fixed the per-row code folds away.
+template <int MR>
 __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int M, int K, int N, int T, int kbw, int grid, float *__restrict__ y,
+    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, float *__restrict__ y,
     int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
+    constexpr int M = MR;
     constexpr int kThreads = kStreamWaves * 64;
     typedef float f4v __attribute__((ext_vector_type(4)));
     typedef uint32_t u2v __attribute__((ext_vector_type(2)));
@@ -677,23 +684,25 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
 
     // table: entry b holds [w0, w1, w2, 0] with w_d = +-C[q][d], q = (b >> 1)
-    // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0
-    static_assert(kCenRows == 1 || kCenRows == 2, "one or two centroid rows per thread");
-    if constexpr (kCenRows == 1) {
-        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + kFusedXF4) : "memory");
-    }
+    // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0.
+    // Thread t writes uint4 t + 1024 i (i < 4), i.e. entry b = t / 16 + 64 i:
+    // q and S0 are the same for its four entries, S1 = i & 1 and S2 = (i >> 1)
+    // xor S0, so the four values are two low halves or-ed with two high ones.
+    static_assert(kCenRows == 1 && kTabWords / 4 / kThreads == 4, "1024 threads build the table in 4 passes");
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    {
+        const uint64_t cv = (((uint64_t)cpair[0].y << 32) | cpair[0].x) >> cshift[0];
+        const uint32_t c0 = (uint32_t)cv & 0xFFu, c1 = (uint32_t)(cv >> 8) & 0xFFu, c2 = (uint32_t)(cv >> 16) & 0xFFu;
+        const bool s0 = (tid >> 4) & 1;
+        const uint32_t w0 = (s0 ? 0u - c0 : c0) & 0xFFu;
+        const uint32_t lo[2] = {w0 | (c1 << 8), w0 | (((0u - c1) & 0xFFu) << 8)};
+        const uint32_t hp = c2 << 16, hn = ((0u - c2) & 0xFFu) << 16;
+        const uint32_t hi[2] = {s0 ? hn : hp, s0 ? hp : hn};  // S2 = (i >> 1) xor S0
 #pragma unroll
-    for (int i = 0; i < kTabWords / 4 / kThreads; ++i) {
-        const int idx = tid + kThreads * i;
-        const int b = idx >> 4, k = i % kCenRows;
-        const uint64_t cv = (((uint64_t)cpair[k].y << 32) | cpair[k].x) >> cshift[k];
-        const int32_t c0 = (int32_t)(cv & 0xFF), c1 = (int32_t)((cv >> 8) & 0xFF), c2 = (int32_t)((cv >> 16) & 0xFF);
-        const int s0 = b & 1, s1 = (b >> 6) & 1, s2 = ((b >> 7) ^ b) & 1;
-        const uint32_t v = (uint32_t)((s0 ? -c0 : c0) & 0xFF) | ((uint32_t)((s1 ? -c1 : c1) & 0xFF) << 8) |
-                           ((uint32_t)((s2 ? -c2 : c2) & 0xFF) << 16);
-        reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t v = lo[i & 1] | hi[i >> 1];
+            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
+        }
     }
 
     // activations landed (only fragment loads behind them)
@@ -701,17 +710,22 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
                  : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3])
                  : "n"(kStreamSlots)
                  : "memory");
+    // (16 waves share a CU's four SIMDs: every VALU operation here costs
+    // four of them, so only the nf4 float4 in use are touched; lanes past
+    // the rows hold zeros)
+    float am[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < kFusedMaxRows; ++r) {
-        if (r < M) {  // uniform
-            float a = 0.0f;
+    for (int i = 0; i < kFusedXF4; ++i) {
+        if (i < nf4) {  // uniform
+            const float a4 = fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w)));
 #pragma unroll
-            for (int i = 0; i < kFusedXF4; ++i)
-                if (i < nf4 && xm[i] == r)
-                    a = fmaxf(a, fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w))));
-            a = wave_max(a);
-            if (lane == 0) rmax[wave * kFusedMaxRows + r] = a;
+            for (int r = 0; r < M; ++r) am[r] = fmaxf(am[r], (M == 1 || xm[i] == r) ? a4 : 0.0f);
         }
+    }
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const float a = wave_max(am[r]);
+        if (lane == 0) rmax[wave * kFusedMaxRows + r] = a;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table, rmax, ybuf complete
 
@@ -729,50 +743,84 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     // below 1 ulp): |t - x / s| < 2.5e-7 |x / s| <= 3.2e-5, so whenever t is
     // more than 1e-4 away from a half-integer, t, the exact quotient and its
     // fp32 rounding lie in the same rounding interval and rint(t) is the
-    // code; otherwise (and for a tiny s) the IEEE quotient decides.
+    // code.  Elements closer to a half-integer (and every element of a row
+    // whose s is below 1e-30) take the IEEE quotient instead, in a pass the
+    // wave runs only when one of its lanes needs it.
     float rcp[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int r = 0; r < kFusedMaxRows; ++r)
-        if (r < M) rcp[r] = srow[r] >= 1e-30f ? __builtin_amdgcn_rcpf(srow[r]) : 0.0f;
-    auto code = [](float xe, float sc, float rc) {
-        float q;
-        const float t = xe * rc;
-        const float qt = rintf(t);
-        if (rc != 0.0f && fabsf(fabsf(t - qt) - 0.5f) > 1e-4f) {
-            q = qt;
-        } else {
-            q = rintf(xe / sc);
-        }
-        return (signed char)fminf(127.0f, fmaxf(-127.0f, q));
-    };
+    for (int r = 0; r < M; ++r) rcp[r] = srow[r] >= 1e-30f ? __builtin_amdgcn_rcpf(srow[r]) : 0.0f;
+    float qv[kFusedXF4][4];
+    float scv[kFusedXF4];
+    uint32_t exact = 0;  // bit 4 i + e: element e of float4 i needs the quotient
 #pragma unroll
     for (int i = 0; i < kFusedXF4; ++i) {
-        if (i < nf4 && xm[i] < M) {
+        scv[i] = 0.0f;
+        if (i < nf4) {  // uniform
             float sc = srow[0], rc = rcp[0];
 #pragma unroll
-            for (int rr = 1; rr < kFusedMaxRows; ++rr) {
+            for (int rr = 1; rr < M; ++rr) {
                 sc = (xm[i] == rr) ? srow[rr] : sc;
                 rc = (xm[i] == rr) ? rcp[rr] : rc;
             }
-            char4 o = make_char4(0, 0, 0, 0);
-            if (sc != 0.0f) {
-                o.x = code(xv[i].x, sc, rc);
-                o.y = code(xv[i].y, sc, rc);
-                o.z = code(xv[i].z, sc, rc);
-                o.w = code(xv[i].w, sc, rc);
+            scv[i] = sc;
+            const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            const bool tiny = rc == 0.0f && sc != 0.0f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float t = xe[e] * rc;
+                qv[i][e] = rintf(t);
+                const bool near = fabsf(fabsf(t - qv[i][e]) - 0.5f) <= 1e-4f || tiny;
+                exact |= (uint32_t)near << (4 * i + e);
             }
-            *reinterpret_cast<char4 *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]) = o;
+        }
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(exact != 0) != 0, 0)) {
+#pragma unroll
+        for (int i = 0; i < kFusedXF4; ++i) {
+            const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (exact & (1u << (4 * i + e))) qv[i][e] = rintf(xe[e] / scv[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kFusedXF4; ++i) {
+        if (i >= nf4) break;  // uniform
+        if (xm[i] < M) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o |= ((uint32_t)(int32_t)__builtin_amdgcn_fmed3f(qv[i][e], -127.0f, 127.0f) & 0xFFu) << (8 * e);
+            *reinterpret_cast<uint32_t *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]) = scv[i] != 0.0f ? o : 0u;
         }
     }
 
-    // A operand: rows < M read their codes (advancing 64 bytes per block),
-    // the other lanes a zero block
-    const int8_t *xa = n < M ? &xw[wave][n * 64 * kbw + g * 16] : zero16;
-    const int xa_step = n < M ? 64 : 0;
+    // The products run without the byte transpose of decode16.  A table
+    // lookup gives the dword [w0, w1, w2, 0] of packed byte k; four of them
+    // (bytes 4j .. 4j + 3 of the lane's 16) are used as they are as the B
+    // operand of one v_mfma_i32_16x16x64_i8, whose 64-deep sum then runs
+    // over (byte, channel) pairs.  A row m = 3r + d (token r, channel d)
+    // carries token r's code of each byte in the channel-d position of its
+    // dword and zeros elsewhere, so D[3r + d][n] = sum_k x_rk w_d(k) for
+    // triple n: four MFMAs per 64 x 16 fragment, one accumulator.
+    //   A lane (m, g): codes of token m / 3 at k = 16 g .. 16 g + 15 of the
+    //   block (rows m >= 3M read a zero block); dword i of A_j is byte i of
+    //   code dword j moved to byte m % 3.
+    const int arw = lane & 15;
+    const bool arow = arw < 3 * M;
+    const int8_t *xa = arow ? &xw[wave][(arw / 3) * 64 * kbw + g * 16] : zero16;
+    const int xa_step = arow ? 64 : 0;
+    uint32_t asel[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t dpos = 8u * (uint32_t)(arw % 3);
+        asel[i] = (0x0C0C0C0Cu & ~(0xFFu << dpos)) | ((uint32_t)i << dpos);
+    }
     const uint32_t lane_off = (uint32_t)lane << 2;
+    const char *tb = reinterpret_cast<const char *>(tab);
     const int nsteps = ntw * kbw;  // fragments per wave
 
-    v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
+    v4i acc = {0, 0, 0, 0};
     int slot = 0, bl = 0, j = 0;
 #pragma unroll 1
     for (int st = 0; st < nsteps; ++st) {
@@ -781,29 +829,30 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
         const v4i a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot read: it may be refilled
         issue_next(slot);
-        v4i b0, b1, b2;
-        decode16(p, lane_off, tab, b0, b1, b2);
-        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b1, acc1, 0, 0, 0);
-        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b2, acc2, 0, 0, 0);
+        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            v4i bq, aq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bq[i] = *reinterpret_cast<const int32_t *>(
+                    tb + __builtin_amdgcn_perm(pw[jj], lane_off, 0x0C0C0400u + ((uint32_t)i << 8)));
+                aq[i] = (int32_t)__builtin_amdgcn_perm(0u, (uint32_t)a[jj], asel[i]);
+            }
+            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, acc, 0, 0, 0);
+        }
         slot = slot == kStreamSlots - 1 ? 0 : slot + 1;
         if (++bl == kbw) {
-            // tile j done for this wave: rows 0..3 sit in lanes 0..15 (g = 0),
-            // element r; channel of (col n, d) within the tile is 3n + d
-            if (g == 0 && kb0 < KB) {
+            // tile j done for this wave: lane (n, g) holds rows 4 g + i,
+            // row m = 3r + d is channel 3n + d of token r within the tile
+            if (kb0 < KB) {
 #pragma unroll
-                for (int r = 0; r < kFusedMaxRows; ++r) {
-                    if (r < M) {
-                        int32_t *yb = &ybuf[(j * kFusedMaxRows + r) * 48 + 3 * n];
-                        atomicAdd(yb + 0, acc0[r]);
-                        atomicAdd(yb + 1, acc1[r]);
-                        atomicAdd(yb + 2, acc2[r]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int m = 4 * g + i;
+                    if (m < 3 * M) atomicAdd(&ybuf[(j * kFusedMaxRows + m / 3) * 48 + 3 * n + m % 3], acc[i]);
                 }
             }
-            acc0 = v4i{0, 0, 0, 0};
-            acc1 = v4i{0, 0, 0, 0};
-            acc2 = v4i{0, 0, 0, 0};
+            acc = v4i{0, 0, 0, 0};
             bl = 0;
             ++j;
         }
@@ -1567,9 +1616,10 @@ bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_
     const int64_t tiles = (T + 15) / 16;
     const int64_t grid = tiles < cus ? tiles : cus;
     if ((tiles + grid - 1) / grid > kStreamMaxTiles) return false;
-    hipLaunchKernelGGL(gemv_stream_kernel, dim3((unsigned)grid), dim3(kStreamWaves * 64), 0, stream, x, tiled,
-                       centroids, scales, (int)M, (int)K, (int)N, (int)T, kbw,
-                       (int)grid, y, acc_out, xq, xs);
+    auto kern = M == 1 ? gemv_stream_kernel<1> : M == 2 ? gemv_stream_kernel<2> : M == 3 ? gemv_stream_kernel<3>
+                                                                                       : gemv_stream_kernel<4>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kStreamWaves * 64), 0, stream, x, tiled, centroids, scales,
+                       (int)K, (int)N, (int)T, kbw, (int)grid, y, acc_out, xq, xs);
     return true;
 }
 
