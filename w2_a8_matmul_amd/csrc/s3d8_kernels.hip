@@ -545,10 +545,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 // stay there until the end; every global store (y, the optional
 // accumulators, xq and xs) happens after the last weight load has landed, so
 // no store enters the vmcnt counts.
-constexpr int kStreamWaves = 16;
-constexpr int kStreamSlots = 4;      // ring slots (1 KiB fragments) per wave
 constexpr int kStreamMaxTiles = 16;  // tiles per workgroup (results held in LDS)
-constexpr int kStreamEp = kStreamMaxTiles * kFusedMaxRows * 48 / (kStreamWaves * 64);  // outputs per thread
 
 // max over each row of 16 lanes, result in every lane of the row (DPP:
 // swap neighbours, swap pairs, mirror halves of 8, mirror the row)
@@ -572,22 +569,26 @@ __device__ __forceinline__ float wave_max(float v) {
 // Arguments used before the first loads come first, so that they are among
 // the kernel arguments preloaded into SGPRs.
 //
-// One instantiation per row count MR: the prologue runs once per launch from
-// a cold instruction cache, so its length in bytes is on the critical path;
-// with the row count fixed the per-row code folds away.
-template <int MR>
-__global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
+// One instantiation per row count MR (the per-row code folds away) and
+// wave count W (8 or 16; the launch uses 16).  Each wave's prologue is a
+// fixed cost that all W waves pay on a CU's four SIMDs.
+template <int MR, int W>
+__global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, float *__restrict__ y,
-    int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, int ntw_q, int ntw_r,
+    float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
     static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
+    static_assert(W == 8 || W == 16, "8 or 16 waves");
     constexpr int M = MR;
-    constexpr int kThreads = kStreamWaves * 64;
+    constexpr int kStreamWaves = W;
+    constexpr int kStreamSlots = 64 / W;  // ring slots (1 KiB fragments) per wave: 64 KiB in all
+    constexpr int kStreamEp = kStreamMaxTiles * kFusedMaxRows * 48 / (W * 64);  // outputs per thread
+    constexpr int kThreads = W * 64;
     typedef float f4v __attribute__((ext_vector_type(4)));
     typedef uint32_t u2v __attribute__((ext_vector_type(2)));
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     __shared__ __attribute__((aligned(16))) uint8_t ring[kStreamWaves][kStreamSlots][1024];
-    __shared__ __attribute__((aligned(16))) int8_t xw[kStreamWaves][1024];
+    __shared__ __attribute__((aligned(16))) int8_t xw[kStreamWaves][16384 / W];
     __shared__ __attribute__((aligned(16))) int8_t zero16[16];
     __shared__ int32_t ybuf[kStreamMaxTiles * kFusedMaxRows * 48];
     __shared__ float rmax[kStreamWaves * kFusedMaxRows];
@@ -598,7 +599,7 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
     const int KB = (K + 63) >> 6;
     const int tiles = (T + 15) >> 4;
     const int kb0 = wave * kbw;
-    const int ntw = (tiles - (int)blockIdx.x + grid - 1) / grid;  // tiles of this workgroup, >= 1
+    const int ntw = ntw_q + ((int)blockIdx.x < ntw_r);  // tiles of this workgroup, >= 1
     const int nout = ntw * M * 48;                                 // outputs of this workgroup
 
     // 1. epilogue scales (the compiler's loads, issued first: the explicit
@@ -646,7 +647,9 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
 #pragma unroll
     for (int i = 0; i < kFusedXF4; ++i) {
         const int f = lane + 64 * i;
-        const int m = (f >= span4) + (f >= 2 * span4) + (f >= 3 * span4) + (f >= 4 * span4);
+        int m = 0;  // row of float4 f; M means past the rows
+#pragma unroll
+        for (int q = 1; q <= M; ++q) m += f >= q * span4;
         const int r = f - m * span4;
         xm[i] = m;
         xr[i] = r;
@@ -685,22 +688,37 @@ __global__ __launch_bounds__(kStreamWaves * 64) void gemv_stream_kernel(
 
     // table: entry b holds [w0, w1, w2, 0] with w_d = +-C[q][d], q = (b >> 1)
     // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0.
-    // Thread t writes uint4 t + 1024 i (i < 4), i.e. entry b = t / 16 + 64 i:
-    // q and S0 are the same for its four entries, S1 = i & 1 and S2 = (i >> 1)
-    // xor S0, so the four values are two low halves or-ed with two high ones.
-    static_assert(kCenRows == 1 && kTabWords / 4 / kThreads == 4, "1024 threads build the table in 4 passes");
-    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    // Thread t writes uint4 t + 64 W i, entry b = t / 16 + 4 W i: bits 0..4
+    // of b come from t (t / 16 < 4 W <= 64), the rest from 4 W i, so S0 is
+    // fixed, q takes kCenRows values and S1, bit 7 depend on i only: every
+    // value is one of two low halves or-ed with one of two high halves of
+    // its centroid row.
+    constexpr int kPasses = kTabWords / 4 / kThreads;
+    static_assert(kCenRows * kThreads == 1024 && kPasses * kThreads == 4096, "table passes");
+    if constexpr (kCenRows == 1) {
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+    }
     {
-        const uint64_t cv = (((uint64_t)cpair[0].y << 32) | cpair[0].x) >> cshift[0];
-        const uint32_t c0 = (uint32_t)cv & 0xFFu, c1 = (uint32_t)(cv >> 8) & 0xFFu, c2 = (uint32_t)(cv >> 16) & 0xFFu;
         const bool s0 = (tid >> 4) & 1;
-        const uint32_t w0 = (s0 ? 0u - c0 : c0) & 0xFFu;
-        const uint32_t lo[2] = {w0 | (c1 << 8), w0 | (((0u - c1) & 0xFFu) << 8)};
-        const uint32_t hp = c2 << 16, hn = ((0u - c2) & 0xFFu) << 16;
-        const uint32_t hi[2] = {s0 ? hn : hp, s0 ? hp : hn};  // S2 = (i >> 1) xor S0
+        uint32_t lo[kCenRows][2], hi[kCenRows][2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t v = lo[i & 1] | hi[i >> 1];
+        for (int k = 0; k < kCenRows; ++k) {
+            const uint64_t cv = (((uint64_t)cpair[k].y << 32) | cpair[k].x) >> cshift[k];
+            const uint32_t c0 = (uint32_t)cv & 0xFFu, c1 = (uint32_t)(cv >> 8) & 0xFFu, c2 = (uint32_t)(cv >> 16) & 0xFFu;
+            const uint32_t w0 = (s0 ? 0u - c0 : c0) & 0xFFu;
+            lo[k][0] = w0 | (c1 << 8);
+            lo[k][1] = w0 | (((0u - c1) & 0xFFu) << 8);
+            const uint32_t hp = c2 << 16, hn = ((0u - c2) & 0xFFu) << 16;
+            hi[k][0] = s0 ? hn : hp;  // bit 7 clear: S2 = S0
+            hi[k][1] = s0 ? hp : hn;
+        }
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            constexpr int P = kThreads / 16;
+            const int hib = P * i;  // bits 5.. of b contributed by the pass
+            const uint32_t v = lo[(hib >> 5) & (kCenRows - 1)][(hib >> 6) & 1] | hi[(hib >> 5) & (kCenRows - 1)][(hib >> 7) & 1];
             reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
         }
     }
@@ -1610,16 +1628,19 @@ bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_
                         const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, float *y,
                         int32_t *acc_out, int cus, hipStream_t stream) {
     if (M < 1 || M > kFusedMaxRows) return false;
-    const int kbw = gemv_kbw((int)K, kStreamWaves);
+    // 16 waves (8 were measured slower at K = 4096: the shorter prologue is
+    // outweighed by half as many waves hiding the decode's LDS latency)
+    constexpr int W = 16;
+    const int kbw = gemv_kbw((int)K, W);
     if (M * kbw > 16) return false;
     const int64_t T = (N + 2) / 3;
     const int64_t tiles = (T + 15) / 16;
     const int64_t grid = tiles < cus ? tiles : cus;
     if ((tiles + grid - 1) / grid > kStreamMaxTiles) return false;
-    auto kern = M == 1 ? gemv_stream_kernel<1> : M == 2 ? gemv_stream_kernel<2> : M == 3 ? gemv_stream_kernel<3>
-                                                                                       : gemv_stream_kernel<4>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kStreamWaves * 64), 0, stream, x, tiled, centroids, scales,
-                       (int)K, (int)N, (int)T, kbw, (int)grid, y, acc_out, xq, xs);
+    auto kern = M == 1 ? gemv_stream_kernel<1, W> : M == 2 ? gemv_stream_kernel<2, W> : M == 3 ? gemv_stream_kernel<3, W>
+                                                                                              : gemv_stream_kernel<4, W>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), 0, stream, x, tiled, centroids, scales, (int)K, (int)N,
+                       (int)T, kbw, (int)grid, (int)(tiles / grid), (int)(tiles % grid), y, acc_out, xq, xs);
     return true;
 }
 
