@@ -190,6 +190,32 @@ def main():
         f"-> {achieved:.1f} GB/s; quant_act alone {qa_mean_us:.2f} us")
     del dP, dX
 
+    # ---------------------------------------------------------------- standalone dequant + copy baselines
+    # the pages' own kernel measurement: S3D8 -> channel-INT8 dequantisation
+    # against a plain copy of the same matrix in INT8, on the c1 gate/up
+    # matrix and on the vision MLP up shape the pages time it on (K=1280,
+    # N=5120); read bandwidth counted on the S3D8 source bytes as there
+    dequant = {}
+    for tag, (Nd, Kd, Pd) in {"c1_gate_up": (N, K, packed),
+                              "vision_mlp_up": (5120, 1280, workloads.uniform_bytes([9, 1], s3d8.num_triples(5120),
+                                                                                     1280))}.items():
+        src = [torch.from_numpy(Pd).to(dev) for _ in range(4)]
+        wout = torch.empty((Nd, Kd), dtype=torch.int8, device=dev)
+        s3d8.dequant(src[0], dC, Nd, w=wout)
+        d_us = graph_launch_us(torch, [lambda r=r: s3d8.dequant(src[r], dC, Nd, w=wout) for r in range(4)], 10)
+        i8 = [torch.empty((Nd, Kd), dtype=torch.int8, device=dev) for _ in range(4)]
+        i8dst = torch.empty((Nd, Kd), dtype=torch.int8, device=dev)
+        c_us = graph_launch_us(torch, [lambda r=r: i8dst.copy_(i8[r]) for r in range(4)], 10)
+        sbytes = s3d8.format_bytes(Nd, Kd)
+        dequant[tag] = {"N": Nd, "K": Kd, "dequant_us": round(d_us, 3),
+                        "dequant_read_GBs": round(sbytes / (d_us * 1e-6) / 1e9, 1),
+                        "dequant_total_GBs": round((s3d8.packed_bytes(Nd, Kd) + Nd * Kd) / (d_us * 1e-6) / 1e9, 1),
+                        "int8_copy_us": round(c_us, 3),
+                        "int8_copy_GBs": round(2 * Nd * Kd / (c_us * 1e-6) / 1e9, 1)}
+        log(f"dequant {tag}: {d_us:.2f} us ({dequant[tag]['dequant_read_GBs']} GB/s on S3D8 bytes); "
+            f"INT8 copy of the same matrix {c_us:.2f} us")
+        del src, wout, i8, i8dst
+
     # ---------------------------------------------------------------- prefill GEMM
     prefill = None
     if not args.no_prefill:
@@ -289,6 +315,7 @@ def main():
                      "algorithmic_bytes": kernel_bytes},
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
+        "dequant": dequant,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
