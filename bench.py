@@ -98,6 +98,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-layer", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +190,50 @@ def main():
     log(f"step {ms_per_step * 1e3:.2f} us -> {value:.1f} GB/s; forward kernel {lin_mean_us:.2f} us "
         f"-> {achieved:.1f} GB/s; quant_act alone {qa_mean_us:.2f} us")
     del dP, dX
+
+    # ---------------------------------------------------------------- one decoder-layer step (c2)
+    # the seven linears of a decoder layer at one token, each with its own
+    # packed weights and activations: seven s3d8_forward launches against
+    # one s3d8_forward_batch launch; effective bytes = the seven matrices'
+    # S3D8 bytes.  Weight copies cycle as above (R2 copies of the layer).
+    layer = None
+    if not args.no_layer:
+        t0 = time.time()
+        mats = []
+        for ln in workloads.C2:
+            Cl, Sl, Pl = s3d8.pack(workloads.weights(ln), seed=ln.pack_seed, max_iters=args.pack_iters)
+            mats.append((ln, Cl, Sl, Pl))
+        log(f"decoder layer packed in {time.time() - t0:.1f}s")
+        layer_bytes = sum(s3d8.format_bytes(ln.N, ln.K) for ln, _, _, _ in mats)
+        R2 = max(2, int(np.ceil(2 * MALL_BYTES / layer_bytes)))
+        lay = []
+        for r in range(R2):
+            items = []
+            for ln, Cl, Sl, Pl in mats:
+                items.append(dict(x=torch.from_numpy(workloads.activations(ln)).to(dev),
+                                  tiled=s3d8.tile(torch.from_numpy(Pl).to(dev), ln.N),
+                                  centroids=torch.from_numpy(Cl).to(dev),
+                                  scales=torch.from_numpy(Sl.view(np.int16)).to(dev), N=ln.N,
+                                  y=torch.empty((ln.M, ln.N), dtype=torch.float32, device=dev),
+                                  xq=torch.empty((ln.M, ln.K), dtype=torch.int8, device=dev),
+                                  xs=torch.empty((ln.M,), dtype=torch.float32, device=dev)))
+            lay.append(items)
+
+        def separate(r):
+            for it in lay[r]:
+                s3d8.forward(it["x"], it["tiled"], it["centroids"], it["scales"], it["N"], y=it["y"], xq=it["xq"],
+                             xs=it["xs"])
+
+        sep_us = graph_launch_us(torch, [lambda r=r: separate(r) for r in range(R2)], 5)
+        bat_us = graph_launch_us(torch, [lambda r=r: s3d8.forward_batch(lay[r]) for r in range(R2)], 5)
+        gbs = layer_bytes / (bat_us * 1e-6) / 1e9
+        layer = {"workload": "c2: q, o 4096x4096; k, v 4096->1024; gate, up 4096->14336; down 14336->4096; M=1",
+                 "effective_weight_bytes": layer_bytes, "separate_launches_us": round(sep_us, 2),
+                 "one_launch_us": round(bat_us, 2), "one_launch_GBs": round(gbs, 1),
+                 "one_launch_frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "weight_copies": R2}
+        log(f"decoder layer: 7 launches {sep_us:.2f} us, one batched launch {bat_us:.2f} us "
+            f"-> {gbs:.1f} GB/s effective weight bytes")
+        del lay
 
     # ---------------------------------------------------------------- standalone dequant + copy baselines
     # the pages' own kernel measurement: S3D8 -> channel-INT8 dequantisation
@@ -315,6 +360,7 @@ def main():
                      "algorithmic_bytes": kernel_bytes},
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
+        "decoder_layer": layer,
         "dequant": dequant,
         "cpu_baseline": cpu,
     }

@@ -194,6 +194,34 @@ int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint
                      const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq,
                      float *xs, int32_t *acc_out, void *stream);
 
+/* One item of s3d8_forward_batch: the arguments of one s3d8_forward call. */
+typedef struct s3d8_forward_item {
+    const float *x;               /* device fp32 [M][K], 16-B aligned, finite */
+    int64_t M, K, N;
+    const uint8_t *tiled;         /* as for s3d8_linear */
+    const uint8_t *centroids;     /* as for s3d8_linear */
+    const uint16_t *scales_bf16;  /* as for s3d8_linear */
+    float *y;                     /* out, device fp32 [M][N] */
+    int8_t *xq;                   /* out, device int8 [M][K], 16-B aligned */
+    float *xs;                    /* out, device fp32 [M] */
+    int32_t *acc_out;             /* optional out, device int32 [M][N] */
+} s3d8_forward_item;
+
+/* Several independent s3d8_forward calls at once, e.g. the seven linears of
+ * a decoder-layer step at one token (each matrix with its own activations,
+ * table and scales).  When 1 <= count <= 8, every item has the same M <= 4
+ * and each matrix fits the streaming GEMV (M * ceil(ceil(K/64)/16) <= 16),
+ * all items run in ONE kernel launch whose workgroups are shared out among
+ * the matrices in proportion to their work; otherwise the items run one
+ * after the other as s3d8_forward calls.  Results are identical to calling
+ * s3d8_forward on each item.  Outputs of different items must not overlap
+ * (items may share x, and then write identical xq / xs).
+ *   count  number of items (0: nothing to do).
+ *   items  host array of count items; read before return, not kept.
+ * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP (as s3d8_forward, for the
+ * first failing item; nothing is launched when validation fails). */
+int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *stream);
+
 /* Size in bytes of the workspace of s3d8_linear_unfused: the whole matrix
  * decoded to channel-INT8 in 2 KiB fragments of 32 channels x 64 columns,
  * ceil(3 * ceil(N/3) / 32) * ceil(K/64) * 2048.  -1 on bad sizes. */

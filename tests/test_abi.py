@@ -151,6 +151,26 @@ def test_linear_unfused_validation():
                                  None) == _lib.S3D8_ERR_SHAPE
 
 
+def test_forward_batch_validation():
+    L = _lib.lib()
+    assert L.s3d8_forward_batch(0, None, None) == 0  # nothing to do, no device touched
+    assert L.s3d8_forward_batch(-1, None, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_forward_batch(1, None, None) == _lib.S3D8_ERR_INVALID_ARG
+    good = dict(x=A16, M=1, K=64, N=9, tiled=A16, centroids=A16, scales_bf16=A16, y=A16, xq=A16, xs=A16,
+                acc_out=None)
+
+    def call(**kw):
+        items = (_lib.ForwardItem * 2)(_lib.ForwardItem(**good), _lib.ForwardItem(**dict(good, **kw)))
+        return L.s3d8_forward_batch(2, ctypes.addressof(items), None)
+
+    assert call(x=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(xs=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(K=40) == _lib.S3D8_ERR_SHAPE
+    assert call(x=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(tiled=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert ctypes.sizeof(_lib.ForwardItem) == 88
+
+
 def test_host_validation_errors():
     W = np.zeros((3, 16), np.float32)
     with pytest.raises(s3d8.S3D8Error) as e:

@@ -311,6 +311,91 @@ def test_forward_decoder_layer(gpu, idx):
     check_y(y, y_r)
 
 
+# ------------------------------------------------------------------ forward_batch
+def _batch_items(specs, gpu):
+    """Device inputs for (x, C, alpha, packed, N) specs."""
+    items = []
+    for x, C, alpha, packed, N in specs:
+        items.append(dict(x=dev(x, gpu), tiled=s3d8.tile(dev(packed, gpu), N), centroids=dev(C, gpu),
+                          scales=dev(alpha.view(np.int16), gpu), N=N))
+    return items
+
+
+def _check_batch(specs, outs):
+    for (x, C, alpha, packed, N), (y, xq, xs, acc) in zip(specs, outs):
+        xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+        np.testing.assert_array_equal(xq.cpu().numpy(), xq_r)
+        np.testing.assert_array_equal(xs.cpu().numpy(), xs_r)
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+        check_y(y.cpu().numpy(), y_r)
+
+
+def test_forward_batch_decoder_layer(gpu):
+    """The seven matrices of one decoder-layer step (q, o, k, v, gate, up,
+    down; down has K = 14336) in one launch, each against the oracle."""
+    specs = []
+    for lin in workloads.C2:
+        C, alpha, packed = packed_matrix(lin)
+        specs.append((workloads.activations(lin), C, alpha, packed, lin.N))
+    outs = s3d8.forward_batch(_batch_items(specs, gpu), return_all=True)
+    torch.cuda.synchronize()
+    _check_batch(specs, outs)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_forward_batch_ragged_shapes(gpu, M):
+    """Mixed K and N (partial triple tiles, K not a multiple of 64, a matrix
+    smaller than one tile) in one launch."""
+    shapes = [(1040, 97), (4096, 1), (80, 50), (16, 3), (256, 385), (2064, 14336)]
+    specs = []
+    for i, (K, N) in enumerate(shapes):
+        C, alpha, packed = random_format([2100, M, i, K, N], N, K)
+        specs.append((workloads.gaussian_matrix([2101, M, i], M, K), C, alpha, packed, N))
+    outs = s3d8.forward_batch(_batch_items(specs, gpu), return_all=True)
+    torch.cuda.synchronize()
+    _check_batch(specs, outs)
+
+
+def test_forward_batch_matches_single_calls(gpu):
+    """Bit-identical to one s3d8_forward per item, also for items sharing x."""
+    M, K = 2, 4096
+    x = workloads.gaussian_matrix([2110], M, K)
+    specs = []
+    for i, N in enumerate([4096, 1024, 1024]):
+        C, alpha, packed = random_format([2111, i], N, K)
+        specs.append((x, C, alpha, packed, N))
+    items = _batch_items(specs, gpu)
+    items[1]["x"] = items[0]["x"]
+    items[2]["x"] = items[0]["x"]
+    outs = s3d8.forward_batch(items, return_all=True)
+    torch.cuda.synchronize()
+    for it, (y, xq, xs, acc) in zip(items, outs):
+        y1, xq1, xs1, acc1 = s3d8.forward(it["x"], it["tiled"], it["centroids"], it["scales"], it["N"],
+                                          return_all=True)
+        torch.cuda.synchronize()
+        for a, b in [(y, y1), (xq, xq1), (xs, xs1), (acc, acc1)]:
+            np.testing.assert_array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+@pytest.mark.parametrize("case", ["nine_items", "mixed_rows", "too_long_k"])
+def test_forward_batch_sequential_fallback(gpu, case):
+    """Item lists the one-launch kernel does not take (more than 8 items,
+    different M, M * ceil(K / 1024) > 16) run as separate launches."""
+    if case == "nine_items":
+        dims = [(1, 64 * (i + 1), 30 + i) for i in range(9)]
+    elif case == "mixed_rows":
+        dims = [(1, 256, 48), (3, 256, 48)]
+    else:
+        dims = [(2, 16384 + 1024, 40), (2, 256, 20)]
+    specs = []
+    for i, (M, K, N) in enumerate(dims):
+        C, alpha, packed = random_format([2120, i, M, K, N], N, K)
+        specs.append((workloads.gaussian_matrix([2121, i], M, K), C, alpha, packed, N))
+    outs = s3d8.forward_batch(_batch_items(specs, gpu), return_all=True)
+    torch.cuda.synchronize()
+    _check_batch(specs, outs)
+
+
 def test_forward_gate_up_m1(gpu):
     lin = workloads.C1[1]
     C, alpha, packed = packed_matrix(lin)

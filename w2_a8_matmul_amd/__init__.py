@@ -228,6 +228,48 @@ def forward(x, tiled, centroids, scales, N: int, y=None, xq=None, xs=None, acc=N
     return y
 
 
+def forward_batch(items, return_all: bool = False):
+    """Several ``forward`` calls in one go (one kernel launch when they fit
+    the streaming GEMV together, see s3d8_forward_batch).  ``items`` is a
+    list of dicts with keys x, tiled, centroids, scales, N and optionally y,
+    xq, xs, acc.  Returns the list of y (or of (y, xq, xs, acc) tuples with
+    ``return_all``)."""
+    torch = _torch()
+    arr = (_lib.ForwardItem * max(1, len(items)))()
+    outs = []
+    dev = None
+    for i, it in enumerate(items):
+        x = it["x"]
+        _dev_check(x, torch.float32, "x")
+        scales = _scales_view(it["scales"])
+        M, K = x.shape
+        N = int(it["N"])
+        _check_weights(it["tiled"], it["centroids"], scales, N, K)
+        if dev is None:
+            dev = x.device
+        elif x.device != dev:
+            raise ValueError("all items must be on one device")
+        y = it.get("y")
+        y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
+        xq = it.get("xq")
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev) if xq is None else xq
+        xs = it.get("xs")
+        xs = torch.empty((M,), dtype=torch.float32, device=dev) if xs is None else xs
+        acc = it.get("acc")
+        if return_all and acc is None:
+            acc = torch.empty((M, N), dtype=torch.int32, device=dev)
+        arr[i] = _lib.ForwardItem(x.data_ptr(), M, K, N, it["tiled"].data_ptr(), it["centroids"].data_ptr(),
+                                  scales.data_ptr(), y.data_ptr(), xq.data_ptr(), xs.data_ptr(),
+                                  acc.data_ptr() if acc is not None else None)
+        outs.append((y, xq, xs, acc, x, scales))
+    if items:
+        with torch.cuda.device(dev):
+            call("s3d8_forward_batch", len(items), ctypes.addressof(arr), _stream(items[0]["x"]))
+    if return_all:
+        return [o[:4] for o in outs]
+    return [o[0] for o in outs]
+
+
 def dequant(packed, centroids, N: int, w=None):
     """Standalone decode to channel-INT8: w int8 [N][K]."""
     torch = _torch()

@@ -566,16 +566,38 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(a, b);
 }
 
-// Arguments used before the first loads come first, so that they are among
-// the kernel arguments preloaded into SGPRs.
+// One launch can serve up to kStreamBatch independent matrices (e.g. the
+// seven linears of a decoder layer, each with its own activations, table
+// and scales): workgroups [wg0[p], wg0[p + 1]) work on matrix p, each on its
+// own tiles, as if launched alone with grid = wg0[p + 1] - wg0[p].  The
+// workgroup starts (first in the arguments, so that they arrive in
+// preloaded SGPRs) pick the matrix; its parameters are then read from the
+// kernel argument segment.
 //
 // One instantiation per row count MR (the per-row code folds away) and
 // wave count W (8 or 16; the launch uses 16).  Each wave's prologue is a
 // fixed cost that all W waves pay on a CU's four SIMDs.
+constexpr int kStreamBatch = 8;
+struct StreamProb {
+    const float *xf;
+    const uint8_t *tiled;
+    const uint8_t *centroids;
+    const uint16_t *scales;
+    float *y;
+    int32_t *acc_out;
+    int8_t *xq_out;
+    float *xs_out;
+    int K, N, T, kbw, ntw_q, ntw_r;  // ntw_q, ntw_r: tiles of the matrix over its workgroups
+};
+struct StreamBatch {
+    int wg0[kStreamBatch + 1];  // first workgroup of each matrix; unused entries INT32_MAX
+    StreamProb p[kStreamBatch];
+};
+
 template <int MR, int W>
-__global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
+__device__ __forceinline__ void gemv_stream_body(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, int ntw_q, int ntw_r,
+    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int bid, int grid, int ntw_q, int ntw_r,
     float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
     static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
     static_assert(W == 8 || W == 16, "8 or 16 waves");
@@ -599,7 +621,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     const int KB = (K + 63) >> 6;
     const int tiles = (T + 15) >> 4;
     const int kb0 = wave * kbw;
-    const int ntw = ntw_q + ((int)blockIdx.x < ntw_r);  // tiles of this workgroup, >= 1
+    const int ntw = ntw_q + (bid < ntw_r);  // tiles of this workgroup, >= 1
     const int nout = ntw * M * 48;                                 // outputs of this workgroup
 
     // 1. epilogue scales (the compiler's loads, issued first: the explicit
@@ -617,7 +639,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
         ep_j[q] = j;
         ep_r[q] = r;
         ep_c[q] = c;
-        const int ch = ((int)blockIdx.x + j * grid) * 48 + c;
+        const int ch = (bid + j * grid) * 48 + c;
         ep_a[q] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (idx < nout && ch < N) ? (uint32_t)ch * 2u : kOOB, 0, 0);
     }
 
@@ -672,7 +694,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     auto issue_next = [&](int slot) {
         const int kb = kb0 + is_b;
         const bool live = is_j < ntw && kb < KB;
-        const uint32_t tile = (uint32_t)((int)blockIdx.x + is_j * grid);
+        const uint32_t tile = (uint32_t)(bid + is_j * grid);
         load_to_lds16(ring_base + 1024u * slot,
                       live ? (tile * (uint32_t)KB + (uint32_t)kb) * 1024u + (uint32_t)lane * 16u : kOOB, rw);
         if (++is_b == kbw) {
@@ -881,7 +903,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
 #pragma unroll
     for (int q = 0; q < kStreamEp; ++q) {
         const int jj = ep_j[q], r = ep_r[q], c = ep_c[q];
-        const int ch = ((int)blockIdx.x + jj * grid) * 48 + c;
+        const int ch = (bid + jj * grid) * 48 + c;
         if (jj < ntw && ch < N) {
             float sx = srow[0];
 #pragma unroll
@@ -891,7 +913,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
             if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
         }
     }
-    if (blockIdx.x == 0) {
+    if (bid == 0) {
         if (tid < M && xs_out) {
             float sx = srow[0];
 #pragma unroll
@@ -908,6 +930,29 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
             }
         }
     }
+}
+
+// One matrix: the arguments used before the first loads come first, so that
+// they are among the kernel arguments preloaded into SGPRs.
+template <int MR, int W>
+__global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
+    const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
+    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, int ntw_q, int ntw_r,
+    float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    gemv_stream_body<MR, W>(xf, tiled, centroids, scales, K, N, T, kbw, (int)blockIdx.x, grid, ntw_q, ntw_r, y,
+                            acc_out, xq_out, xs_out);
+}
+
+// Several matrices: this workgroup's matrix is the last p with wg0[p] <=
+// blockIdx.x; its parameters come from the argument segment.
+template <int MR, int W>
+__global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamBatch B) {
+    int pi = 0;
+#pragma unroll
+    for (int q = 1; q < kStreamBatch; ++q) pi += (int)blockIdx.x >= B.wg0[q];
+    const StreamProb &P = B.p[pi];
+    gemv_stream_body<MR, W>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, P.T, P.kbw, (int)blockIdx.x - B.wg0[pi],
+                            B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
 }
 
 // --------------------------------------------------------------- GEMM
@@ -1624,24 +1669,83 @@ int64_t tiled_bytes(int64_t N, int64_t K) { return ((N + 2) / 3 + 15) / 16 * ((K
 // The streaming fused GEMV takes M <= 4 rows whose per-wave activation slice
 // fits four float4 per lane, and at most kStreamMaxTiles tiles per workgroup
 // (one workgroup per CU).  Returns false (launching nothing) otherwise.
-bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_t K, int64_t N,
-                        const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, float *y,
-                        int32_t *acc_out, int cus, hipStream_t stream) {
+// Workgroups for a batch of stream-GEMV matrices: one per CU in all, shared
+// out so that the largest per-workgroup work (tiles x K) is smallest; each
+// matrix gets at least one workgroup and at most one per tile.  Returns
+// false if some matrix would need more than kStreamMaxTiles tiles on one
+// workgroup.
+bool stream_split(int count, const int64_t *tiles, const int64_t *K, int cus, int *groups) {
+    int used = 0;
+    for (int p = 0; p < count; ++p) {
+        groups[p] = 1;
+        ++used;
+    }
+    auto load = [&](int p, int g) { return (tiles[p] + g - 1) / g * K[p]; };
+    while (used < cus) {
+        int best = -1;
+        for (int p = 0; p < count; ++p)
+            if (groups[p] < tiles[p] && (best < 0 || load(p, groups[p]) > load(best, groups[best]))) best = p;
+        if (best < 0) break;
+        ++groups[best];
+        ++used;
+    }
+    for (int p = 0; p < count; ++p)
+        if ((tiles[p] + groups[p] - 1) / groups[p] > kStreamMaxTiles) return false;
+    return true;
+}
+
+// One launch of gemv_stream_kernel over `count` matrices that share M; false
+// (nothing launched) if a matrix does not fit the kernel.
+bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus, hipStream_t stream) {
+    if (count < 1 || count > kStreamBatch) return false;
+    const int64_t M = items[0].M;
     if (M < 1 || M > kFusedMaxRows) return false;
     // 16 waves (8 were measured slower at K = 4096: the shorter prologue is
     // outweighed by half as many waves hiding the decode's LDS latency)
     constexpr int W = 16;
-    const int kbw = gemv_kbw((int)K, W);
-    if (M * kbw > 16) return false;
-    const int64_t T = (N + 2) / 3;
-    const int64_t tiles = (T + 15) / 16;
-    const int64_t grid = tiles < cus ? tiles : cus;
-    if ((tiles + grid - 1) / grid > kStreamMaxTiles) return false;
-    auto kern = M == 1 ? gemv_stream_kernel<1, W> : M == 2 ? gemv_stream_kernel<2, W> : M == 3 ? gemv_stream_kernel<3, W>
-                                                                                              : gemv_stream_kernel<4, W>;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(W * 64), 0, stream, x, tiled, centroids, scales, (int)K, (int)N,
-                       (int)T, kbw, (int)grid, (int)(tiles / grid), (int)(tiles % grid), y, acc_out, xq, xs);
+    int64_t tiles[kStreamBatch], Ks[kStreamBatch];
+    for (int p = 0; p < count; ++p) {
+        if (items[p].M != M || M * gemv_kbw((int)items[p].K, W) > 16) return false;
+        tiles[p] = ((items[p].N + 2) / 3 + 15) / 16;
+        Ks[p] = items[p].K;
+    }
+    int groups[kStreamBatch];
+    if (!stream_split(count, tiles, Ks, cus, groups)) return false;
+    StreamBatch B;
+    int wg = 0;
+    for (int p = 0; p < kStreamBatch; ++p) {
+        B.wg0[p] = p < count ? wg : INT32_MAX;
+        if (p >= count) {
+            B.p[p] = StreamProb{};
+            continue;
+        }
+        const s3d8_forward_item &it = items[p];
+        B.p[p] = StreamProb{it.x, it.tiled, it.centroids, it.scales_bf16, it.y, it.acc_out, it.xq, it.xs,
+                            (int)it.K, (int)it.N, (int)((it.N + 2) / 3), gemv_kbw((int)it.K, W),
+                            (int)(tiles[p] / groups[p]), (int)(tiles[p] % groups[p])};
+        wg += groups[p];
+    }
+    for (int p = count; p <= kStreamBatch; ++p) B.wg0[p] = INT32_MAX;
+    B.wg0[count] = wg;  // end of the last matrix
+    if (count == 1) {
+        const StreamProb &P = B.p[0];
+        auto kern = M == 1 ? gemv_stream_kernel<1, W> : M == 2 ? gemv_stream_kernel<2, W>
+                  : M == 3 ? gemv_stream_kernel<3, W> : gemv_stream_kernel<4, W>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf, P.tiled, P.centroids, P.scales, P.K,
+                           P.N, P.T, P.kbw, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
+        return true;
+    }
+    auto kern = M == 1 ? gemv_stream_batch_kernel<1, W> : M == 2 ? gemv_stream_batch_kernel<2, W>
+              : M == 3 ? gemv_stream_batch_kernel<3, W> : gemv_stream_batch_kernel<4, W>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)wg), dim3(W * 64), 0, stream, B);
     return true;
+}
+
+bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_t K, int64_t N,
+                        const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, float *y,
+                        int32_t *acc_out, int cus, hipStream_t stream) {
+    const s3d8_forward_item it{x, M, K, N, tiled, centroids, scales, y, xq, xs, acc_out};
+    return launch_gemv_stream_batch(1, &it, cus, stream);
 }
 
 }  // namespace
@@ -1765,6 +1869,29 @@ int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint
     rc = s3d8_quant_act(x, M, K, xq, xs, stream);
     if (rc) return rc;
     return s3d8_linear(xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, stream);
+}
+
+int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *stream) {
+    if (count < 0 || (count > 0 && !items)) return s3d8::fail(S3D8_ERR_INVALID_ARG, "bad item list");
+    for (int32_t i = 0; i < count; ++i) {
+        const s3d8_forward_item &it = items[i];
+        if (!it.x || !it.xq || !it.xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+        int rc = check_linear_args(it.tiled, it.centroids, it.scales_bf16, it.y, it.M, it.K, it.N);
+        if (rc) return rc;
+        if (!aligned16(it.x) || !aligned16(it.xq)) return s3d8::fail(S3D8_ERR_ALIGN, "x and xq must be 16-byte aligned");
+    }
+    if (count == 0) return S3D8_OK;
+    int cus = 0;
+    int rc = check_device(&cus);
+    if (rc) return rc;
+    if (launch_gemv_stream_batch(count, items, cus, (hipStream_t)stream)) return launch_status();
+    for (int32_t i = 0; i < count; ++i) {
+        const s3d8_forward_item &it = items[i];
+        rc = s3d8_forward(it.x, it.M, it.K, it.N, it.tiled, it.centroids, it.scales_bf16, it.y, it.xq, it.xs,
+                          it.acc_out, stream);
+        if (rc) return rc;
+    }
+    return S3D8_OK;
 }
 
 int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
