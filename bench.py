@@ -261,6 +261,21 @@ def main():
             f"INT8 copy of the same matrix {c_us:.2f} us")
         del src, wout, i8, i8dst
 
+    # ---------------------------------------------------------------- frozen-centroid encode on the device
+    # (the quantiser in front of the path): c1 gate/up fp32 weights with the
+    # table the packer fitted, against the host encoder on the same input
+    Wd = torch.from_numpy(workloads.weights(lin)).to(dev)
+    s3d8.encode_device(Wd, dC)
+    e_us = graph_launch_us(torch, [lambda: s3d8.encode_device(Wd, dC)], 3)
+    t0 = time.perf_counter()
+    s3d8.encode(workloads.weights(lin), C)
+    host_s = time.perf_counter() - t0
+    encode = {"workload": f"{lin.name} weights fp32 [{N}][{K}]", "device_us": round(e_us, 1),
+              "fp32_read_GBs": round(4 * N * K / (e_us * 1e-6) / 1e9, 1), "host_s": round(host_s, 3)}
+    log(f"device encode {lin.name}: {e_us:.1f} us ({encode['fp32_read_GBs']} GB/s of fp32 weights); "
+        f"host encode {host_s:.3f} s")
+    del Wd
+
     # ---------------------------------------------------------------- prefill GEMM
     prefill = None
     if not args.no_prefill:
@@ -361,6 +376,7 @@ def main():
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
         "decoder_layer": layer,
+        "encode": encode,
         "dequant": dequant,
         "cpu_baseline": cpu,
     }

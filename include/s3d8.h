@@ -222,6 +222,23 @@ typedef struct s3d8_forward_item {
  * first failing item; nothing is launched when validation fails). */
 int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *stream);
 
+/* The frozen-centroid quantiser of s3d8_encode on the GPU ([PAPER] Sec. 3.4
+ * "Quantization", the QAT-phase Q(.)), with the same arithmetic and the
+ * same results: alpha_i = bf16_rne(fp32(max_j |W_ij|) / 127.0f) (0 for
+ * padded channels), W' = |W| / alpha in fp64, q = the first centroid row at
+ * the smallest squared distance, signs S_d = (W < 0), bytes per the [BLOG]
+ * bit layout.  Two launches on `stream`.
+ *   W            device fp32 [N][K] row-major, 4-B aligned, finite.
+ *   centroids    device uint8 [32][3]; every entry must be <= 127 (not
+ *                checked: the table is in device memory).
+ *   scales_bf16  out, device uint16 [3*ceil(N/3)], 2-B aligned.
+ *   packed       out, device uint8 [ceil(N/3)][K] (canonical layout; pass
+ *                it to s3d8_tile for the kernels' layout).
+ * Errors: INVALID_ARG, SHAPE (K % 16 != 0, or N*K over 2^31), ALIGN,
+ * DEVICE, HIP. */
+int32_t s3d8_encode_device(const float *W, int64_t N, int64_t K, const uint8_t *centroids,
+                           uint16_t *scales_bf16, uint8_t *packed, void *stream);
+
 /* Size in bytes of the workspace of s3d8_linear_unfused: the whole matrix
  * decoded to channel-INT8 in 2 KiB fragments of 32 channels x 64 columns,
  * ceil(3 * ceil(N/3) / 32) * ceil(K/64) * 2048.  -1 on bad sizes. */

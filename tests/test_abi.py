@@ -171,6 +171,16 @@ def test_forward_batch_validation():
     assert ctypes.sizeof(_lib.ForwardItem) == 88
 
 
+def test_encode_device_validation():
+    L = _lib.lib()
+    assert L.s3d8_encode_device(None, 3, 16, A16, A16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_encode_device(A16, 3, 24, A16, A16, A16, None) == _lib.S3D8_ERR_SHAPE
+    assert L.s3d8_encode_device(A16 + 2, 3, 16, A16, A16, A16, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_encode_device(A16, 3, 16, A16, A_ODD, A16, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_encode_device(A16, 0, 16, A16, A16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_encode_device(A16, 1 << 20, 1 << 12, A16, A16, A16, None) == _lib.S3D8_ERR_SHAPE
+
+
 def test_host_validation_errors():
     W = np.zeros((3, 16), np.float32)
     with pytest.raises(s3d8.S3D8Error) as e:

@@ -311,6 +311,39 @@ def test_forward_decoder_layer(gpu, idx):
     check_y(y, y_r)
 
 
+# ------------------------------------------------------------------ encode on the device
+@pytest.mark.parametrize("N,K", [(1, 16), (3, 16), (7, 48), (100, 64), (385, 1040), (1282, 4096)])
+def test_encode_device_matches_oracle(gpu, N, K):
+    """Scales and bytes bit-exact, with a zero channel, -0.0, tiny and large
+    entries and ties (duplicate centroid rows)."""
+    C = workloads.uniform_centroids([2130, N, K], 0, 127)
+    C[5] = C[3]  # duplicate rows: the lower index must win
+    W = workloads.gaussian_matrix([2131, N, K], N, K, 0.02)
+    W[0, 0] = -0.0
+    W[0, 1] = 1e-39  # subnormal
+    if N > 2:
+        W[2, :] = 0.0
+    if N > 5:
+        W[5, 3] = 40.0
+    sc, pk = s3d8.encode_device(dev(W, gpu), dev(C, gpu))
+    torch.cuda.synchronize()
+    s_or, p_or = oracle.encode(W, C)
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint16), s_or)
+    np.testing.assert_array_equal(pk.cpu().numpy(), p_or)
+
+
+def test_encode_device_c1_gate_up(gpu):
+    """The full gate/up weight matrix with the table the packer fits for it:
+    the device encode reproduces the packer's bytes and scales."""
+    lin = workloads.C1[1]
+    W = workloads.weights(lin)
+    C, alpha, packed = packed_matrix(lin)
+    sc, pk = s3d8.encode_device(dev(W, gpu), dev(C, gpu))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sc.cpu().numpy().view(np.uint16), alpha)
+    np.testing.assert_array_equal(pk.cpu().numpy(), packed)
+
+
 # ------------------------------------------------------------------ forward_batch
 def _batch_items(specs, gpu):
     """Device inputs for (x, C, alpha, packed, N) specs."""

@@ -270,6 +270,22 @@ def forward_batch(items, return_all: bool = False):
     return [o[0] for o in outs]
 
 
+def encode_device(W, centroids):
+    """Frozen-centroid encode on the GPU (same results as ``encode``):
+    returns (scales bf16 bits as int16 [3T], packed uint8 [T][K])."""
+    torch = _torch()
+    _dev_check(W, torch.float32, "W")
+    _dev_check(centroids, torch.uint8, "centroids")
+    N, K = W.shape
+    T = num_triples(N)
+    scales = torch.empty((3 * T,), dtype=torch.int16, device=W.device)
+    packed = torch.empty((T, K), dtype=torch.uint8, device=W.device)
+    with torch.cuda.device(W.device):
+        call("s3d8_encode_device", W.data_ptr(), N, K, centroids.data_ptr(), scales.data_ptr(), packed.data_ptr(),
+             _stream(W))
+    return scales, packed
+
+
 def dequant(packed, centroids, N: int, w=None):
     """Standalone decode to channel-INT8: w int8 [N][K]."""
     torch = _torch()

@@ -41,6 +41,7 @@ SIGNATURES = {
     "s3d8_unfused_workspace_bytes": (_I64, [_I64, _I64]),
     "s3d8_linear_unfused": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
     "s3d8_forward_batch": (_I32, [_I32, _P, _P]),
+    "s3d8_encode_device": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
 }
 
 

@@ -1573,9 +1573,83 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     store_tile_rows<false, kAcc>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
+// --------------------------------------------------------------- encode on the device
+
+// The frozen-centroid quantiser of the paper (Sec. 3.4, "Quantization", the
+// QAT-phase Q(.)) on the GPU, with the same arithmetic as the host encoder:
+// alpha_i = bf16_rne(fp32(max_j |W_ij|) / 127.0f); W'_{t,j,d} = |W_{3t+d,j}|
+// / alpha in fp64 (0 for padded channels and zero scales); q = the first
+// centroid row with the smallest squared distance (components summed in
+// order 0, 1, 2, no fused multiply-add); S_d = W < 0; byte per the blog's
+// "Bit layout".
+
+// One workgroup per (padded) channel row: the absmax and its bf16 scale.
+constexpr int kScaleThreads = 256;
+__global__ __launch_bounds__(kScaleThreads) void channel_scale_kernel(const float *__restrict__ W, int N, int K,
+                                                                      uint16_t *__restrict__ alpha) {
+    __shared__ float red[kScaleThreads / 64];
+    const int i = blockIdx.x;
+    float a = 0.0f;
+    if (i < N)
+        for (int j = threadIdx.x; j < K; j += kScaleThreads) a = fmaxf(a, fabsf(W[(int64_t)i * K + j]));
+    a = wave_max(a);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = red[0];
+#pragma unroll
+        for (int w = 1; w < kScaleThreads / 64; ++w) m = fmaxf(m, red[w]);
+        const float s = m / 127.0f;  // IEEE division
+        const uint32_t u = __float_as_uint(s);
+        // round to nearest even on the upper 16 bits (s is finite and >= 0)
+        alpha[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+    }
+}
+
+// One thread per packed byte (triple t, column j).
+constexpr int kEncodeThreads = 256;
+__global__ __launch_bounds__(kEncodeThreads) void encode_kernel(const float *__restrict__ W, int N, int K, int T,
+                                                                const uint16_t *__restrict__ alpha,
+                                                                const uint8_t *__restrict__ centroids,
+                                                                uint8_t *__restrict__ packed) {
+    __shared__ double cent[96];
+    if (threadIdx.x < 96) cent[threadIdx.x] = (double)centroids[threadIdx.x];
+    __syncthreads();
+    const int64_t p = (int64_t)blockIdx.x * kEncodeThreads + threadIdx.x;
+    if (p >= (int64_t)T * K) return;
+    const int t = (int)(p / K), j = (int)(p - (int64_t)t * K);
+    double x[3];
+    uint32_t sg[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const int i = 3 * t + d;
+        x[d] = 0.0;
+        sg[d] = 0;
+        if (i < N) {
+            const float w = W[(int64_t)i * K + j];
+            sg[d] = w < 0.0f ? 1u : 0u;
+            const double a = (double)bf16_to_f32(alpha[i]);
+            if (a != 0.0) x[d] = fabs((double)w) / a;
+        }
+    }
+    double best = 0.0;
+    uint32_t q = 0;
+#pragma unroll 4
+    for (int l = 0; l < 32; ++l) {
+        const double e0 = cent[3 * l] - x[0], e1 = cent[3 * l + 1] - x[1], e2 = cent[3 * l + 2] - x[2];
+        const double dd = e0 * e0 + e1 * e1 + e2 * e2;
+        if (l == 0 || dd < best) {
+            best = dd;
+            q = (uint32_t)l;
+        }
+    }
+    packed[p] = (uint8_t)(sg[0] | (q << 1) | (sg[1] << 6) | ((sg[2] ^ sg[0]) << 7));
+}
+
 // --------------------------------------------------------------- host glue
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t lim_int() { return (int64_t(1) << 31) - 1; }
 
 int check_sizes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return s3d8::fail(S3D8_ERR_INVALID_ARG, "sizes must be positive");
@@ -1892,6 +1966,27 @@ int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *
         if (rc) return rc;
     }
     return S3D8_OK;
+}
+
+int32_t s3d8_encode_device(const float *W, int64_t N, int64_t K, const uint8_t *centroids, uint16_t *scales_bf16,
+                           uint8_t *packed, void *stream) {
+    if (!W || !centroids || !scales_bf16 || !packed) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_sizes(1, K, N);
+    if (rc) return rc;
+    if (reinterpret_cast<uintptr_t>(W) & 3u) return s3d8::fail(S3D8_ERR_ALIGN, "W must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(scales_bf16) & 1u)
+        return s3d8::fail(S3D8_ERR_ALIGN, "scales_bf16 must be 2-byte aligned");
+    if (N > lim_int() / K) return s3d8::fail(S3D8_ERR_SHAPE, "N * K over 2^31");
+    rc = check_device(nullptr);
+    if (rc) return rc;
+    const int64_t T = (N + 2) / 3;
+    hipLaunchKernelGGL(channel_scale_kernel, dim3((unsigned)(3 * T)), dim3(kScaleThreads), 0, (hipStream_t)stream, W,
+                       (int)N, (int)K, scales_bf16);
+    const int64_t nbytes = T * K;
+    hipLaunchKernelGGL(encode_kernel, dim3((unsigned)((nbytes + kEncodeThreads - 1) / kEncodeThreads)),
+                       dim3(kEncodeThreads), 0, (hipStream_t)stream, W, (int)N, (int)K, (int)T, scales_bf16, centroids,
+                       packed);
+    return launch_status();
 }
 
 int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
