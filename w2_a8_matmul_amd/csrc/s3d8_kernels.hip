@@ -530,21 +530,19 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 // decode is, and how evenly the bytes are spread.  Every wave issues, before
 // anything else, one load of the centroid row its lanes need for the table,
 // its share of the fp32 activations, and its first kStreamSlots weight
-// fragments (1 KiB each, buffer loads straight into a private LDS ring, no
-// registers).  The table is then built from registers, the row absmax is
-// reduced with DPP, and one barrier later the activations are quantised and
-// the decode starts.  The main loop has no barriers: each wave waits for its
-// own ring slot (an explicit vmcnt count: the compiler does not see these
-// loads), decodes it, runs three v_mfma_i32_16x16x64_i8 (token rows as the A
-// operand, rows >= M read a zero block) and refills the slot four fragments
-// ahead.
+// fragments (16 bytes per lane each, a ring of registers: a lane's bytes are
+// its own, so they need not pass through LDS).  The table is then built from
+// registers, the row absmax is reduced with DPP, and one barrier later the
+// activations are quantised and the decode starts.  The main loop has no
+// barriers: each step takes the oldest fragment, refills its ring entry
+// kStreamSlots steps ahead, looks up the 16 packed bytes and runs four
+// v_mfma_i32_16x16x64_i8 on the raw lookup dwords (see the loop).
 //
-// Work split: a workgroup takes tiles of 16 triples (blockIdx.x, + grid,
+// Work split: a workgroup takes tiles of 16 triples (its index, + grid,
 // ...), its 16 waves split K into ranges of kbw 64-column blocks.  Partial
 // sums of a tile meet in LDS through integer atomics (exact, order-free) and
 // stay there until the end; every global store (y, the optional
-// accumulators, xq and xs) happens after the last weight load has landed, so
-// no store enters the vmcnt counts.
+// accumulators, xq and xs) happens after the last weight load has landed.
 constexpr int kStreamMaxTiles = 16;  // tiles per workgroup (results held in LDS)
 
 // max over each row of 16 lanes, result in every lane of the row (DPP:
@@ -603,13 +601,12 @@ __device__ __forceinline__ void gemv_stream_body(
     static_assert(W == 8 || W == 16, "8 or 16 waves");
     constexpr int M = MR;
     constexpr int kStreamWaves = W;
-    constexpr int kStreamSlots = 64 / W;  // ring slots (1 KiB fragments) per wave: 64 KiB in all
+    constexpr int kStreamSlots = 64 / W;  // fragments in flight per wave (registers)
     constexpr int kStreamEp = kStreamMaxTiles * kFusedMaxRows * 48 / (W * 64);  // outputs per thread
     constexpr int kThreads = W * 64;
     typedef float f4v __attribute__((ext_vector_type(4)));
     typedef uint32_t u2v __attribute__((ext_vector_type(2)));
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kStreamWaves][kStreamSlots][1024];
     __shared__ __attribute__((aligned(16))) int8_t xw[kStreamWaves][16384 / W];
     __shared__ __attribute__((aligned(16))) int8_t zero16[16];
     __shared__ int32_t ybuf[kStreamMaxTiles * kFusedMaxRows * 48];
@@ -686,24 +683,27 @@ __device__ __forceinline__ void gemv_stream_body(
     // fragment load does
     asm volatile("s_barrier" ::: "memory");
 
-    // 4. weight fragments: step s of this wave = tile j = s / kbw of the
-    //    workgroup, block kb0 + s % kbw; steps past the end read nothing
-    const v4i rw = rsrc_words(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
-    const uint32_t ring_base = S3D8_LDS_OFFSET(&ring[wave][0][0]);
+    // 4. weight fragments, straight into registers (each lane's 16 bytes of
+    //    a fragment are its own: nothing to share through LDS): step s of
+    //    this wave = tile j = s / kbw of the workgroup, block kb0 + s % kbw,
+    //    kStreamSlots steps in flight in a ring of registers; steps past the
+    //    end read zeros (out-of-range offsets)
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
     int is_j = 0, is_b = 0;  // (tile, block) of the next step to issue
-    auto issue_next = [&](int slot) {
+    auto next_off = [&]() {
         const int kb = kb0 + is_b;
         const bool live = is_j < ntw && kb < KB;
         const uint32_t tile = (uint32_t)(bid + is_j * grid);
-        load_to_lds16(ring_base + 1024u * slot,
-                      live ? (tile * (uint32_t)KB + (uint32_t)kb) * 1024u + (uint32_t)lane * 16u : kOOB, rw);
+        const uint32_t off = live ? (tile * (uint32_t)KB + (uint32_t)kb) * 1024u + (uint32_t)lane * 16u : kOOB;
         if (++is_b == kbw) {
             is_b = 0;
             ++is_j;
         }
+        return off;
     };
+    uint4 pr[kStreamSlots];
 #pragma unroll
-    for (int sl = 0; sl < kStreamSlots; ++sl) issue_next(sl);
+    for (int sl = 0; sl < kStreamSlots; ++sl) pr[sl] = bload16(rw, next_off());
 
     for (int i = tid; i < kStreamMaxTiles * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
@@ -861,40 +861,42 @@ __device__ __forceinline__ void gemv_stream_body(
     const int nsteps = ntw * kbw;  // fragments per wave
 
     v4i acc = {0, 0, 0, 0};
-    int slot = 0, bl = 0, j = 0;
+    int bl = 0, j = 0;
 #pragma unroll 1
-    for (int st = 0; st < nsteps; ++st) {
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStreamSlots - 1) : "memory");  // this step's fragment landed
-        const uint4 p = *reinterpret_cast<const uint4 *>(&ring[wave][slot][16 * lane]);
-        const v4i a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slot read: it may be refilled
-        issue_next(slot);
-        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+    for (int st0 = 0; st0 < nsteps; st0 += kStreamSlots) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            v4i bq, aq;
+        for (int u = 0; u < kStreamSlots; ++u) {
+            if (st0 + u >= nsteps) break;  // uniform
+            const uint4 p = pr[u];
+            pr[u] = bload16(rw, next_off());
+            v4i a = {0, 0, 0, 0};
+            if (arow) a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);  // 3M of 16 rows in use
+            const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                bq[i] = *reinterpret_cast<const int32_t *>(
-                    tb + __builtin_amdgcn_perm(pw[jj], lane_off, 0x0C0C0400u + ((uint32_t)i << 8)));
-                aq[i] = (int32_t)__builtin_amdgcn_perm(0u, (uint32_t)a[jj], asel[i]);
-            }
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, acc, 0, 0, 0);
-        }
-        slot = slot == kStreamSlots - 1 ? 0 : slot + 1;
-        if (++bl == kbw) {
-            // tile j done for this wave: lane (n, g) holds rows 4 g + i,
-            // row m = 3r + d is channel 3n + d of token r within the tile
-            if (kb0 < KB) {
+            for (int jj = 0; jj < 4; ++jj) {
+                v4i bq, aq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int m = 4 * g + i;
-                    if (m < 3 * M) atomicAdd(&ybuf[(j * kFusedMaxRows + m / 3) * 48 + 3 * n + m % 3], acc[i]);
+                    bq[i] = *reinterpret_cast<const int32_t *>(
+                        tb + __builtin_amdgcn_perm(pw[jj], lane_off, 0x0C0C0400u + ((uint32_t)i << 8)));
+                    aq[i] = (int32_t)__builtin_amdgcn_perm(0u, (uint32_t)a[jj], asel[i]);
                 }
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, acc, 0, 0, 0);
             }
-            acc = v4i{0, 0, 0, 0};
-            bl = 0;
-            ++j;
+            if (++bl == kbw) {
+                // tile j done for this wave: lane (n, g) holds rows 4 g + i,
+                // row m = 3r + d is channel 3n + d of token r within the tile
+                if (kb0 < KB) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int m = 4 * g + i;
+                        if (m < 3 * M) atomicAdd(&ybuf[(j * kFusedMaxRows + m / 3) * 48 + 3 * n + m % 3], acc[i]);
+                    }
+                }
+                acc = v4i{0, 0, 0, 0};
+                bl = 0;
+                ++j;
+            }
         }
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
