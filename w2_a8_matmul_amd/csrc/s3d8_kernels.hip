@@ -21,6 +21,7 @@
 // exactly the INT8 operand layout of the MFMA instructions.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <cstring>
@@ -592,13 +593,14 @@ struct StreamBatch {
     StreamProb p[kStreamBatch];
 };
 
-template <int MR, int W>
+template <int MR, int W, int NF>
 __device__ __forceinline__ void gemv_stream_body(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
     const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int bid, int grid, int ntw_q, int ntw_r,
     float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
     static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
     static_assert(W == 8 || W == 16, "8 or 16 waves");
+    static_assert(NF >= 1 && NF <= kFusedXF4, "1 to 4 float4 of activations per lane");
     constexpr int M = MR;
     constexpr int kStreamWaves = W;
     constexpr int kStreamSlots = 64 / W;  // fragments in flight per wave (registers)
@@ -661,10 +663,10 @@ __device__ __forceinline__ void gemv_stream_body(
     const v4i rx = rsrc_words(xf, (uint32_t)M * (uint32_t)K * 4u);
     const int span4 = 16 * kbw;
     const int nf4 = (M * span4 + 63) >> 6;  // float4 per lane in use (<= 4)
-    f4v xv[kFusedXF4];
-    int xm[kFusedXF4], xr[kFusedXF4];
+    f4v xv[NF];
+    int xm[NF], xr[NF];
 #pragma unroll
-    for (int i = 0; i < kFusedXF4; ++i) {
+    for (int i = 0; i < NF; ++i) {
         const int f = lane + 64 * i;
         int m = 0;  // row of float4 f; M means past the rows
 #pragma unroll
@@ -718,9 +720,9 @@ __device__ __forceinline__ void gemv_stream_body(
     constexpr int kPasses = kTabWords / 4 / kThreads;
     static_assert(kCenRows * kThreads == 1024 && kPasses * kThreads == 4096, "table passes");
     if constexpr (kCenRows == 1) {
-        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + NF) : "memory");
     } else {
-        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + kFusedXF4) : "memory");
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + NF) : "memory");
     }
     {
         const bool s0 = (tid >> 4) & 1;
@@ -746,16 +748,22 @@ __device__ __forceinline__ void gemv_stream_body(
     }
 
     // activations landed (only fragment loads behind them)
-    asm volatile("s_waitcnt vmcnt(%4)"
-                 : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3])
-                 : "n"(kStreamSlots)
-                 : "memory");
+    if constexpr (NF == 1) {
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(xv[0]) : "n"(kStreamSlots) : "memory");
+    } else if constexpr (NF == 2) {
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(xv[0]), "+v"(xv[1]) : "n"(kStreamSlots) : "memory");
+    } else if constexpr (NF == 3) {
+        asm volatile("s_waitcnt vmcnt(%3)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]) : "n"(kStreamSlots) : "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(%4)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]) : "n"(kStreamSlots)
+                     : "memory");
+    }
     // (16 waves share a CU's four SIMDs: every VALU operation here costs
     // four of them, so only the nf4 float4 in use are touched; lanes past
     // the rows hold zeros)
     float am[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < kFusedXF4; ++i) {
+    for (int i = 0; i < NF; ++i) {
         if (i < nf4) {  // uniform
             const float a4 = fmaxf(fmaxf(fabsf(xv[i].x), fabsf(xv[i].y)), fmaxf(fabsf(xv[i].z), fabsf(xv[i].w)));
 #pragma unroll
@@ -789,11 +797,11 @@ __device__ __forceinline__ void gemv_stream_body(
     float rcp[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < M; ++r) rcp[r] = srow[r] >= 1e-30f ? __builtin_amdgcn_rcpf(srow[r]) : 0.0f;
-    float qv[kFusedXF4][4];
-    float scv[kFusedXF4];
+    float qv[NF][4];
+    float scv[NF];
     uint32_t exact = 0;  // bit 4 i + e: element e of float4 i needs the quotient
 #pragma unroll
-    for (int i = 0; i < kFusedXF4; ++i) {
+    for (int i = 0; i < NF; ++i) {
         scv[i] = 0.0f;
         if (i < nf4) {  // uniform
             float sc = srow[0], rc = rcp[0];
@@ -816,7 +824,7 @@ __device__ __forceinline__ void gemv_stream_body(
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(exact != 0) != 0, 0)) {
 #pragma unroll
-        for (int i = 0; i < kFusedXF4; ++i) {
+        for (int i = 0; i < NF; ++i) {
             const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -824,7 +832,7 @@ __device__ __forceinline__ void gemv_stream_body(
         }
     }
 #pragma unroll
-    for (int i = 0; i < kFusedXF4; ++i) {
+    for (int i = 0; i < NF; ++i) {
         if (i >= nf4) break;  // uniform
         if (xm[i] < M) {
             uint32_t o = 0;
@@ -924,7 +932,7 @@ __device__ __forceinline__ void gemv_stream_body(
         }
         if (xq_out) {
 #pragma unroll
-            for (int i = 0; i < kFusedXF4; ++i) {
+            for (int i = 0; i < NF; ++i) {
                 const int k = kb0 * 64 + 4 * xr[i];
                 if (i < nf4 && xm[i] < M && k < K)
                     *reinterpret_cast<char4 *>(xq_out + (int64_t)xm[i] * K + k) =
@@ -936,24 +944,24 @@ __device__ __forceinline__ void gemv_stream_body(
 
 // One matrix: the arguments used before the first loads come first, so that
 // they are among the kernel arguments preloaded into SGPRs.
-template <int MR, int W>
+template <int MR, int W, int NF>
 __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
     const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, int ntw_q, int ntw_r,
     float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
-    gemv_stream_body<MR, W>(xf, tiled, centroids, scales, K, N, T, kbw, (int)blockIdx.x, grid, ntw_q, ntw_r, y,
+    gemv_stream_body<MR, W, NF>(xf, tiled, centroids, scales, K, N, T, kbw, (int)blockIdx.x, grid, ntw_q, ntw_r, y,
                             acc_out, xq_out, xs_out);
 }
 
 // Several matrices: this workgroup's matrix is the last p with wg0[p] <=
 // blockIdx.x; its parameters come from the argument segment.
-template <int MR, int W>
+template <int MR, int W, int NF>
 __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamBatch B) {
     int pi = 0;
 #pragma unroll
     for (int q = 1; q < kStreamBatch; ++q) pi += (int)blockIdx.x >= B.wg0[q];
     const StreamProb &P = B.p[pi];
-    gemv_stream_body<MR, W>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, P.T, P.kbw, (int)blockIdx.x - B.wg0[pi],
+    gemv_stream_body<MR, W, NF>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, P.T, P.kbw, (int)blockIdx.x - B.wg0[pi],
                             B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
 }
 
@@ -1803,16 +1811,28 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     }
     for (int p = count; p <= kStreamBatch; ++p) B.wg0[p] = INT32_MAX;
     B.wg0[count] = wg;  // end of the last matrix
+    // float4 of activations per lane: ceil(M * kbw / 4) for the widest K
+    int NF = 1;
+    for (int p = 0; p < count; ++p) NF = std::max(NF, (int)((M * B.p[p].kbw + 3) / 4));
+    typedef void (*Single)(const float *, const uint8_t *, const uint8_t *, const uint16_t *, int, int, int, int, int,
+                           int, int, float *, int32_t *, int8_t *, float *);
+    typedef void (*Batched)(StreamBatch);
+#define S3D8_ROW(m) {gemv_stream_kernel<m, W, 1>, gemv_stream_kernel<m, W, 2>, gemv_stream_kernel<m, W, 3>, \
+                      gemv_stream_kernel<m, W, 4>}
+    static const Single single[4][4] = {S3D8_ROW(1), S3D8_ROW(2), S3D8_ROW(3), S3D8_ROW(4)};
+#undef S3D8_ROW
+#define S3D8_ROW(m) {gemv_stream_batch_kernel<m, W, 1>, gemv_stream_batch_kernel<m, W, 2>, \
+                      gemv_stream_batch_kernel<m, W, 3>, gemv_stream_batch_kernel<m, W, 4>}
+    static const Batched batched[4][4] = {S3D8_ROW(1), S3D8_ROW(2), S3D8_ROW(3), S3D8_ROW(4)};
+#undef S3D8_ROW
     if (count == 1) {
         const StreamProb &P = B.p[0];
-        auto kern = M == 1 ? gemv_stream_kernel<1, W> : M == 2 ? gemv_stream_kernel<2, W>
-                  : M == 3 ? gemv_stream_kernel<3, W> : gemv_stream_kernel<4, W>;
-        hipLaunchKernelGGL(kern, dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf, P.tiled, P.centroids, P.scales, P.K,
-                           P.N, P.T, P.kbw, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
+        hipLaunchKernelGGL(single[M - 1][NF - 1], dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf, P.tiled,
+                           P.centroids, P.scales, P.K, P.N, P.T, P.kbw, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out,
+                           P.xs_out);
         return true;
     }
-    auto kern = M == 1 ? gemv_stream_batch_kernel<1, W> : M == 2 ? gemv_stream_batch_kernel<2, W>
-              : M == 3 ? gemv_stream_batch_kernel<3, W> : gemv_stream_batch_kernel<4, W>;
+    auto kern = batched[M - 1][NF - 1];
     hipLaunchKernelGGL(kern, dim3((unsigned)wg), dim3(W * 64), 0, stream, B);
     return true;
 }
