@@ -876,7 +876,6 @@ __device__ __forceinline__ void gemv_stream_body(
         for (int u = 0; u < kStreamSlots; ++u) {
             if (st0 + u >= nsteps) break;  // uniform
             const uint4 p = pr[u];
-            pr[u] = bload16(rw, next_off());
             v4i a = {0, 0, 0, 0};
             if (arow) a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);  // 3M of 16 rows in use
             const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
@@ -891,6 +890,9 @@ __device__ __forceinline__ void gemv_stream_body(
                 }
                 acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, acc, 0, 0, 0);
             }
+            // refill the entry once its bytes are consumed (so the new load
+            // writes the same registers and the loop carries no copies)
+            pr[u] = bload16(rw, next_off());
             if (++bl == kbw) {
                 // tile j done for this wave: lane (n, g) holds rows 4 g + i,
                 // row m = 3r + d is channel 3n + d of token r within the tile
