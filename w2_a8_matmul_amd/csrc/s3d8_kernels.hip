@@ -596,15 +596,17 @@ struct StreamBatch {
 template <int MR, int W, int NF>
 __device__ __forceinline__ void gemv_stream_body(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int bid, int grid, int ntw_q, int ntw_r,
+    const uint16_t *__restrict__ scales, int K, int N, int bid, int grid, int ntw_q, int ntw_r,
     float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
     static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
+    const int T = (N + 2) / 3;
+    const int kbw = (((K + 63) >> 6) + W - 1) / W;  // 64-column blocks per wave
     static_assert(W == 8 || W == 16, "8 or 16 waves");
     static_assert(NF >= 1 && NF <= kFusedXF4, "1 to 4 float4 of activations per lane");
     constexpr int M = MR;
     constexpr int kStreamWaves = W;
     constexpr int kStreamSlots = 64 / W;  // fragments in flight per wave (registers)
-    constexpr int kStreamEp = kStreamMaxTiles * kFusedMaxRows * 48 / (W * 64);  // outputs per thread
+    constexpr int kStreamEp = (kStreamMaxTiles * MR * 48 + W * 64 - 1) / (W * 64);  // outputs per thread
     constexpr int kThreads = W * 64;
     typedef float f4v __attribute__((ext_vector_type(4)));
     typedef uint32_t u2v __attribute__((ext_vector_type(2)));
@@ -707,7 +709,7 @@ __device__ __forceinline__ void gemv_stream_body(
 #pragma unroll
     for (int sl = 0; sl < kStreamSlots; ++sl) pr[sl] = bload16(rw, next_off());
 
-    for (int i = tid; i < kStreamMaxTiles * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
+    for (int i = tid; i < ntw * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
 
     // table: entry b holds [w0, w1, w2, 0] with w_d = +-C[q][d], q = (b >> 1)
@@ -949,10 +951,10 @@ __device__ __forceinline__ void gemv_stream_body(
 template <int MR, int W, int NF>
 __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int K, int N, int T, int kbw, int grid, int ntw_q, int ntw_r,
-    float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
-    gemv_stream_body<MR, W, NF>(xf, tiled, centroids, scales, K, N, T, kbw, (int)blockIdx.x, grid, ntw_q, ntw_r, y,
-                            acc_out, xq_out, xs_out);
+    const uint16_t *__restrict__ scales, int K, int N, int grid, int ntw_q, int ntw_r, float *__restrict__ y,
+    int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    gemv_stream_body<MR, W, NF>(xf, tiled, centroids, scales, K, N, (int)blockIdx.x, grid, ntw_q, ntw_r, y, acc_out,
+                                xq_out, xs_out);
 }
 
 // Several matrices: this workgroup's matrix is the last p with wg0[p] <=
@@ -963,7 +965,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamB
 #pragma unroll
     for (int q = 1; q < kStreamBatch; ++q) pi += (int)blockIdx.x >= B.wg0[q];
     const StreamProb &P = B.p[pi];
-    gemv_stream_body<MR, W, NF>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, P.T, P.kbw, (int)blockIdx.x - B.wg0[pi],
+    gemv_stream_body<MR, W, NF>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, (int)blockIdx.x - B.wg0[pi],
                             B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
 }
 
@@ -1817,7 +1819,7 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     int NF = 1;
     for (int p = 0; p < count; ++p) NF = std::max(NF, (int)((M * B.p[p].kbw + 3) / 4));
     typedef void (*Single)(const float *, const uint8_t *, const uint8_t *, const uint16_t *, int, int, int, int, int,
-                           int, int, float *, int32_t *, int8_t *, float *);
+                           float *, int32_t *, int8_t *, float *);
     typedef void (*Batched)(StreamBatch);
 #define S3D8_ROW(m) {gemv_stream_kernel<m, W, 1>, gemv_stream_kernel<m, W, 2>, gemv_stream_kernel<m, W, 3>, \
                       gemv_stream_kernel<m, W, 4>}
@@ -1830,8 +1832,7 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     if (count == 1) {
         const StreamProb &P = B.p[0];
         hipLaunchKernelGGL(single[M - 1][NF - 1], dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf, P.tiled,
-                           P.centroids, P.scales, P.K, P.N, P.T, P.kbw, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out,
-                           P.xs_out);
+                           P.centroids, P.scales, P.K, P.N, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
         return true;
     }
     auto kern = batched[M - 1][NF - 1];
