@@ -23,6 +23,12 @@ Parity status of each function (what pins it, in ``tests/test_oracle_pins.py``):
                                   planted scales)
   encode                          pinned (brute-force argmin on tiny inputs,
                                   sign rule, planted recovery)
+  decode_3d8 / decode_weight_3d8  pinned (a 3D8 table holding the S3D8 decode of
+                                  every byte reproduces the S3D8 decode; numpy
+                                  fancy indexing of distinct-valued tables)
+  linear_acc_decoded              pinned (numpy int64 matmul)
+  to_bf16                         pinned (torch bfloat16 conversion; ties to
+                                  even on constructed half-way values)
   fit_centroids                   invariants only: integer centroids in
                                   [0,127], non-increasing Lloyd distortion,
                                   exact planted recovery.  Fit quality on
@@ -74,6 +80,10 @@ def _load():
         "oracle_byte_from_fields": (ctypes.c_uint8, [I32, I32, I32, I32]),
         "oracle_decode_weight": (I32, [P, P, I64, I64, I64]),
         "oracle_decode": (None, [P, P, I64, I64, P]),
+        "oracle_decode_weight_3d8": (I32, [P, P, I64, I64, I64]),
+        "oracle_decode_3d8": (None, [P, P, I64, I64, P]),
+        "oracle_linear_acc_decoded": (I32, [P, I64, I64, I64, P, P]),
+        "oracle_to_bf16": (None, [P, I64, P]),
         "oracle_quant_act": (None, [P, I64, I64, P, P]),
         "oracle_acc_one": (I64, [P, P, P, I64, I64]),
         "oracle_linear_acc": (I32, [P, I64, I64, I64, P, P, P]),
@@ -157,6 +167,22 @@ def decode(packed, C, N: int, K: int) -> np.ndarray:
     return w
 
 
+def decode_weight_3d8(packed, T3, K: int, i: int, j: int) -> int:
+    packed = _c(packed, np.uint8)
+    T3 = _c(T3, np.int8)
+    return int(_load().oracle_decode_weight_3d8(_p(packed), _p(T3), K, i, j))
+
+
+def decode_3d8(packed, T3, N: int, K: int) -> np.ndarray:
+    """3D8 (blog "S3D8 design notes"): w[3t+d][j] = T3[packed[t][j]][d], int8 [N][K]."""
+    packed = _c(packed, np.uint8)
+    T3 = _c(T3, np.int8)
+    assert packed.size == num_triples(N) * K and T3.size == 768
+    w = np.empty((N, K), np.int8)
+    _load().oracle_decode_3d8(_p(packed), _p(T3), N, K, _p(w))
+    return w
+
+
 # ---------------------------------------------------------------- activations
 def quant_act(x):
     """Per-token absmax INT8: returns (xq int8 [M][K], xs fp32 [M])."""
@@ -189,6 +215,34 @@ def linear_acc(xq, packed, C, N: int) -> np.ndarray:
     if bad:
         raise ArithmeticError("accumulator outside K*127^2")
     return acc
+
+
+def linear_acc_decoded(xq, w) -> np.ndarray:
+    """Naive int dot products of xq [M][K] with a decoded int8 matrix w [N][K]."""
+    xq = _c(xq, np.int8)
+    w = _c(w, np.int8)
+    M, K = xq.shape
+    N = w.shape[0]
+    assert w.shape == (N, K)
+    acc = np.empty((M, N), np.int32)
+    bad = _load().oracle_linear_acc_decoded(_p(xq), M, K, N, _p(w), _p(acc))
+    if bad:
+        raise ArithmeticError("accumulator outside K*127^2")
+    return acc
+
+
+def linear_acc_3d8(xq, packed, T3, N: int) -> np.ndarray:
+    """INT32 products with 3D8 weights: decode, then plain dot products."""
+    xq = _c(xq, np.int8)
+    return linear_acc_decoded(xq, decode_3d8(packed, T3, N, xq.shape[1]))
+
+
+def to_bf16(y) -> np.ndarray:
+    """bf16 output of the blog's kernel: RNE of each fp32 result (uint16 bits)."""
+    y = _c(y, np.float32)
+    out = np.empty(y.shape, np.uint16)
+    _load().oracle_to_bf16(_p(y), y.size, _p(out))
+    return out
 
 
 def epilogue(acc, xs, alpha_bf16, N: int) -> np.ndarray:

@@ -35,7 +35,11 @@
  *   - nearest-centroid ties go to the lowest index;
  *   - k-means++ draws come from SplitMix64 (counter form); Lloyd stops when
  *     no assignment changes or after max_iters; an empty cluster keeps its
- *     centroid; centroids are rounded half-to-even and clamped to [0,127].
+ *     centroid; centroids are rounded half-to-even and clamped to [0,127];
+ *   - 3D8 (the unstructured format the blog compares S3D8 with) keeps S3D8's
+ *     channel packing, scales and matrix layout; its table is int8 [256][3],
+ *     row-major, entries in [-127, 127], and the whole byte is the row index;
+ *   - bfloat16 output is the round-to-nearest-even of the fp32 epilogue value.
  */
 #include <math.h>
 #include <stdint.h>
@@ -119,6 +123,32 @@ void oracle_decode(const uint8_t *packed, const uint8_t *C, int64_t N, int64_t K
 }
 
 /* ------------------------------------------------------------------ */
+/* 3D8: the unstructured 3-weights-per-byte format                     */
+/* ------------------------------------------------------------------ */
+
+/* [BLOG] "S3D8: a 2.7-bit weight format for fast decoding" and "S3D8
+ * design notes": the plain 3-values-per-byte vector format uses the whole
+ * byte as an 8-bit index into a (256, 3) table of signed values (768
+ * bytes), with no separate sign selectors.  Channel packing, scales and
+ * the packed matrix layout are those of S3D8; only the byte -> weights
+ * step differs:  w_ij = T[b][i mod 3], b = packed[floor(i/3)][j], with T
+ * row-major int8 [256][3]. */
+int32_t oracle_decode_weight_3d8(const uint8_t *packed, const int8_t *T3, int64_t K,
+                                 int64_t i, int64_t j) {
+    int64_t t = i / 3;
+    int32_t d = (int32_t)(i % 3);
+    uint8_t b = packed[t * K + j];
+    return (int32_t)T3[(int64_t)b * 3 + d];
+}
+
+/* The whole 3D8 matrix, one weight at a time: w is [N][K] int8. */
+void oracle_decode_3d8(const uint8_t *packed, const int8_t *T3, int64_t N, int64_t K, int8_t *w) {
+    for (int64_t i = 0; i < N; ++i)
+        for (int64_t j = 0; j < K; ++j)
+            w[i * K + j] = (int8_t)oracle_decode_weight_3d8(packed, T3, K, i, j);
+}
+
+/* ------------------------------------------------------------------ */
 /* Activation quantisation (per-token channel-scaled INT8)             */
 /* ------------------------------------------------------------------ */
 
@@ -191,6 +221,27 @@ int32_t oracle_linear_acc(const int8_t *xq, int64_t M, int64_t K, int64_t N,
     return bad;
 }
 
+/* acc[M][N] = xq[M][K] . w[N][K]^T for an already decoded int8 weight
+ * matrix (any format), summed in int64; returns 1 if some |acc| exceeds
+ * K*127*127, else 0. */
+int32_t oracle_linear_acc_decoded(const int8_t *xq, int64_t M, int64_t K, int64_t N,
+                                  const int8_t *w, int32_t *acc) {
+    const int64_t bound = K * 127 * 127;
+    int32_t bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t *wrow = w + n * K;
+        for (int64_t m = 0; m < M; ++m) {
+            int64_t s = 0;
+            const int8_t *xr = xq + m * K;
+            for (int64_t j = 0; j < K; ++j) s += (int64_t)xr[j] * (int64_t)wrow[j];
+            if (s > bound || s < -bound) bad |= 1;
+            acc[m * N + n] = (int32_t)s;
+        }
+    }
+    return bad;
+}
+
 /* [BLOG] "Fused matrix-vector product": y = x_s * float(acc) * float(W_s),
  * evaluated left to right in fp32 with the bf16 channel scale widened to
  * fp32.  y is [M][N]. */
@@ -203,6 +254,13 @@ void oracle_epilogue(const int32_t *acc, const float *xs, const uint16_t *alpha_
             volatile float r = t * oracle_bf16_to_f32(alpha_bf16[n]);
             y[m * N + n] = r;
         }
+}
+
+/* [BLOG] "Fused matrix-vector product": the blog's kernel converts each
+ * fp32 result to bfloat16 on the way out.  y16[e] = bf16_rne(y[e]) for the
+ * fp32 epilogue values y (round to nearest even, as the conversion above). */
+void oracle_to_bf16(const float *y, int64_t n, uint16_t *y16) {
+    for (int64_t e = 0; e < n; ++e) y16[e] = oracle_f32_to_bf16_rne(y[e]);
 }
 
 /* ------------------------------------------------------------------ */

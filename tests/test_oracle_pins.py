@@ -500,3 +500,71 @@ def test_encode_decode_idempotent():
     alpha2, packed2 = oracle.encode(W2, C)
     np.testing.assert_array_equal(alpha2, alpha)
     np.testing.assert_array_equal(oracle.decode(packed2, C, 9, 32), w)
+
+
+# ------------------------------------------------------------------ 3D8 and bf16 output
+# Blog "S3D8: a 2.7-bit weight format for fast decoding": 3D8 is the plain
+# format with a (256, 3) table of signed values indexed by the whole byte;
+# S3D8's 256 signed centroids are the 8 sign reflections of its 32
+# absolute-value rows.  Blog "Fused matrix-vector product": results are
+# converted to bfloat16 on the way out.
+def test_3d8_with_multiplied_out_s3d8_table_reproduces_s3d8():
+    """A 3D8 table whose row b is the S3D8 decode of byte b (from the
+    signed-LUT reading, not from the oracle) decodes any matrix exactly as
+    S3D8 does."""
+    K, N = 48, 17
+    packed = workloads.uniform_bytes([910], oracle.num_triples(N), K)
+    for C in _tables():
+        T3 = np.array([_signed_lut_decode(b, C) for b in range(256)], np.int8)
+        np.testing.assert_array_equal(oracle.decode_3d8(packed, T3, N, K), oracle.decode(packed, C, N, K))
+
+
+def test_3d8_decode_is_row_lookup_numpy():
+    """w[3t+d][j] = T[packed[t][j]][d], checked with numpy fancy indexing; the
+    table's entries differ along both axes, so reading it transposed, or
+    mapping channel i to a component other than i mod 3, fails."""
+    T3 = workloads.signed_table([911])
+    assert (T3[:, 0] != T3[:, 1]).any() and (T3[:255] != T3[1:]).any()
+    K, N = 40, 14  # ragged: 5 triples, the last with 2 real channels
+    packed = workloads.uniform_bytes([912], oracle.num_triples(N), K)
+    w = oracle.decode_3d8(packed, T3, N, K)
+    ref = T3[packed].transpose(0, 2, 1).reshape(-1, K)[:N]
+    np.testing.assert_array_equal(w, ref)
+    for i, j in [(0, 0), (4, 7), (13, 39), (12, 1)]:
+        assert oracle.decode_weight_3d8(packed, T3, K, i, j) == int(T3[packed[i // 3, j], i % 3])
+
+
+def test_linear_acc_decoded_matches_numpy_matmul():
+    g = np.random.Generator(np.random.PCG64(913))
+    M, K, N = 5, 96, 13
+    xq = g.integers(-127, 128, size=(M, K)).astype(np.int8)
+    w = g.integers(-127, 128, size=(N, K)).astype(np.int8)
+    acc = oracle.linear_acc_decoded(xq, w)
+    np.testing.assert_array_equal(acc, xq.astype(np.int64) @ w.astype(np.int64).T)
+    # the 3D8 product: decode by numpy indexing, multiply by numpy
+    T3 = workloads.signed_table([914])
+    packed = workloads.uniform_bytes([915], oracle.num_triples(N), K)
+    wd = T3[packed].transpose(0, 2, 1).reshape(-1, K)[:N].astype(np.int64)
+    np.testing.assert_array_equal(oracle.linear_acc_3d8(xq, packed, T3, N), xq.astype(np.int64) @ wd.T)
+    # extremes: all +-127 stays within K * 127^2 and is exact
+    xq_max = np.full((1, K), -127, np.int8)
+    T_max = np.full((256, 3), -127, np.int8)
+    assert (oracle.linear_acc_3d8(xq_max, packed, T_max, N) == K * 127 * 127).all()
+
+
+def test_to_bf16_matches_torch_and_scalar():
+    import torch
+
+    g = np.random.Generator(np.random.PCG64(916))
+    vals = np.concatenate([
+        g.standard_normal(3000).astype(np.float32) * np.float32(40.0),
+        g.lognormal(-8, 4, 991).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, 1e-40, -3.0e38], np.float32),
+        # exact ties (lower half 0x8000) with even and odd upper halves
+        np.array([0x3F808000, 0x3F818000, 0xC0008000, 0x00018000], np.uint32).view(np.float32),
+    ]).reshape(40, -1)
+    ours = oracle.to_bf16(vals)
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(ours.reshape(-1)[:200], oracle.f32_to_bf16(vals.reshape(-1)[:200]))
+    assert list(oracle.to_bf16(np.array([0x3F808000, 0x3F818000], np.uint32).view(np.float32))) == [0x3F80, 0x3F82]

@@ -129,3 +129,10 @@ def uniform_bytes(seed_words, rows: int, cols: int) -> np.ndarray:
 def uniform_centroids(seed_words, lo: int = 1, hi: int = 127) -> np.ndarray:
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_words))))
     return g.integers(lo, hi + 1, size=(32, 3), dtype=np.uint8)
+
+
+def signed_table(seed_words, lo: int = -127, hi: int = 127) -> np.ndarray:
+    """int8 [256][3], uniform integers in [lo, hi]: a 3D8 table of signed
+    centroids (one row per byte value)."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(seed_words))))
+    return g.integers(lo, hi + 1, size=(256, 3)).astype(np.int8)
