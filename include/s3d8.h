@@ -276,6 +276,69 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
 int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K,
                      int8_t *w, void *stream);
 
+/* ------------------------------------------------------- format variants */
+
+/* Weight formats.  Both store three weights of channels 3t, 3t+1, 3t+2 per
+ * byte in the same packed / tiled layout, with the same bf16 channel scales;
+ * they differ in the table that turns a byte into three INT8 weights.
+ *   S3D8_FORMAT_S3D8  table = uint8 [32][3] absolute-value centroids; the
+ *                     byte holds a 5-bit row index and three sign selectors
+ *                     (see "Format" above).
+ *   S3D8_FORMAT_3D8   table = int8 [256][3] signed centroids, row-major,
+ *                     768 bytes, entries in [-127, 127]; the whole byte is
+ *                     the row index: w_{3t+d, j} = table[b][d].  This is the
+ *                     unstructured 3-values-per-byte format that [BLOG]
+ *                     "S3D8: a 2.7-bit weight format for fast decoding"
+ *                     compares S3D8 with (256 signed centroids; S3D8's are
+ *                     the 8 sign reflections of 32 absolute ones). */
+#define S3D8_FORMAT_S3D8 0
+#define S3D8_FORMAT_3D8 1
+
+/* Output types of the linear layer.
+ *   S3D8_OUT_F32   y fp32 [M][N] (as s3d8_linear).
+ *   S3D8_OUT_BF16  y bfloat16 bit patterns, uint16 [M][N]: each fp32 result
+ *                  of "Linear" rounded to nearest even, as the [BLOG] fused
+ *                  matrix-vector listing converts its results on the way
+ *                  out. */
+#define S3D8_OUT_F32 0
+#define S3D8_OUT_BF16 1
+
+/* s3d8_linear for either weight format and either output type.
+ *   table      device, 4-B aligned: the format's table (96 or 768 bytes).
+ *   format     S3D8_FORMAT_S3D8 or S3D8_FORMAT_3D8.
+ *   y          out, device [M][N] of fp32 or bf16 (per out_type).
+ *   out_type   S3D8_OUT_F32 or S3D8_OUT_BF16.
+ *   the rest   as for s3d8_linear (acc_out stays int32).
+ * Errors: as s3d8_linear; INVALID_ARG also for an unknown format or output
+ * type.  With S3D8_FORMAT_S3D8 and S3D8_OUT_F32 it is s3d8_linear. */
+int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                       const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
+                       int32_t *acc_out, void *stream);
+
+/* s3d8_forward for either weight format and either output type (arguments
+ * as s3d8_linear_ex and s3d8_forward; xq and xs as for s3d8_forward).  The
+ * same launches as s3d8_forward.  Errors: as s3d8_forward, plus
+ * INVALID_ARG for an unknown format or output type. */
+int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
+                        int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type, int8_t *xq, float *xs,
+                        int32_t *acc_out, void *stream);
+
+/* s3d8_linear_unfused for either weight format and either output type
+ * (arguments as s3d8_linear_ex, workspace as s3d8_linear_unfused).
+ * Errors: as s3d8_linear_unfused, plus INVALID_ARG for an unknown format or
+ * output type. */
+int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                               const uint8_t *tiled, const void *table, int32_t format, const uint16_t *scales_bf16,
+                               void *y, int32_t out_type, int32_t *acc_out, int8_t *workspace,
+                               int64_t workspace_bytes, void *stream);
+
+/* s3d8_dequant for either weight format: w = the table decode of every
+ * byte, channel-INT8 [N][K] (padded channels not written).  table and
+ * format as for s3d8_linear_ex; the rest as for s3d8_dequant.  Errors: as
+ * s3d8_dequant, plus INVALID_ARG for an unknown format. */
+int32_t s3d8_dequant_ex(const uint8_t *packed, const void *table, int32_t format, int64_t N, int64_t K, int8_t *w,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -212,3 +212,52 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(ImportError):
         _lib.lib()
+
+
+def test_variant_entry_points_validation():
+    """The format / output-type entry points reject unknown variants and
+    validate like the entry points they extend, before any GPU work."""
+    L = _lib.lib()
+
+    def lin(fmt=0, out=0, **kw):
+        a = dict(xq=A16, xs=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, acc=None)
+        a.update(kw)
+        return L.s3d8_linear_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"], a["y"],
+                                out, a["acc"], None)
+
+    assert lin(fmt=2) == _lib.S3D8_ERR_INVALID_ARG
+    assert lin(fmt=-1) == _lib.S3D8_ERR_INVALID_ARG
+    assert lin(out=2) == _lib.S3D8_ERR_INVALID_ARG
+    assert "format" in L.s3d8_last_error().decode() or "output" in L.s3d8_last_error().decode()
+    assert lin(fmt=1, out=1, y=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert lin(fmt=1, K=40) == _lib.S3D8_ERR_SHAPE
+    assert lin(fmt=1, C=A16 + 2) == _lib.S3D8_ERR_ALIGN
+    assert lin(out=1, t=A_ODD) == _lib.S3D8_ERR_ALIGN
+
+    def fwd(fmt=0, out=0, **kw):
+        a = dict(x=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, xq=A16, xs=A16, acc=None)
+        a.update(kw)
+        return L.s3d8_forward_ex(a["x"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"], a["y"], out,
+                                 a["xq"], a["xs"], a["acc"], None)
+
+    assert fwd(fmt=7) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(out=-1) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(fmt=1, x=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert fwd(fmt=1, out=1, x=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert fwd(fmt=1, K=8) == _lib.S3D8_ERR_SHAPE
+
+    def unf(fmt=0, out=0, **kw):
+        a = dict(xq=A16, xs=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, acc=None, ws=A16, wb=1 << 20)
+        a.update(kw)
+        return L.s3d8_linear_unfused_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"],
+                                        a["y"], out, a["acc"], a["ws"], a["wb"], None)
+
+    assert unf(fmt=3) == _lib.S3D8_ERR_INVALID_ARG
+    assert unf(out=5) == _lib.S3D8_ERR_INVALID_ARG
+    assert unf(fmt=1, wb=16) == _lib.S3D8_ERR_INVALID_ARG
+    assert unf(out=1, ws=None) == _lib.S3D8_ERR_INVALID_ARG
+
+    assert L.s3d8_dequant_ex(A16, A16, 2, 9, 64, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_dequant_ex(A16, None, 1, 9, 64, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_dequant_ex(A16, A16 + 2, 1, 9, 64, A16, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_dequant_ex(A16, A16, 1, 9, 24, A16, None) == _lib.S3D8_ERR_SHAPE

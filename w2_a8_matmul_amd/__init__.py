@@ -8,7 +8,10 @@ is missing, importing ``w2_a8_matmul_amd._lib`` raises.
 
 Format: the S3D8 storage format of "Llama-Mobile: Efficient 2.7-Bit
 Quantization of VLMs" (Sec. 3.4, Eq. 1) with the byte layout of the blog
-"11 billion parameters on a phone" ("Bit layout").
+"11 billion parameters on a phone" ("Bit layout").  The device functions also
+take 3D8 weights (``fmt="3d8"``: the table is int8 [256][3] signed
+centroids indexed by the whole byte, the format the blog sets beside S3D8)
+and write bf16 outputs (``out="bf16"``, as the blog's fused kernel does).
 """
 from __future__ import annotations
 
@@ -138,32 +141,63 @@ def _scales_view(scales):
     return scales
 
 
-def _check_weights(tiled, centroids, scales, N, K):
+_FORMATS = {"s3d8": 0, "3d8": 1}
+_OUTS = {"f32": 0, "bf16": 1}
+
+
+def _variant(fmt: str, out: str = "f32"):
+    if fmt not in _FORMATS or out not in _OUTS:
+        raise ValueError(f"fmt must be one of {list(_FORMATS)}, out one of {list(_OUTS)}")
+    return _FORMATS[fmt], _OUTS[out]
+
+
+def _table_view(table, fmt: str):
+    """S3D8: uint8 [32][3] centroids; 3D8: int8 [256][3] signed table (uint8 views accepted)."""
+    torch = _torch()
+    if fmt == "3d8" and table.dtype == torch.int8:
+        table = table.view(torch.uint8)
+    _dev_check(table, torch.uint8, "centroids" if fmt == "s3d8" else "table")
+    if table.numel() != (96 if fmt == "s3d8" else 768):
+        raise ValueError("table size does not match the format")
+    return table
+
+
+def _check_weights(tiled, centroids, scales, N, K, fmt: str = "s3d8"):
     torch = _torch()
     _dev_check(tiled, torch.uint8, "tiled")
-    _dev_check(centroids, torch.uint8, "centroids")
+    _table_view(centroids, fmt)
     T = num_triples(N)
-    if tiled.numel() < tiled_bytes(N, K) or centroids.numel() != 96 or scales.numel() < 3 * T:
+    if tiled.numel() < tiled_bytes(N, K) or scales.numel() < 3 * T:
         raise ValueError("tiled / centroids / scales do not match (N, K)")
 
 
-def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False):
-    """Fused S3D8 linear on pre-quantised activations: y fp32 [M][N] (and
-    the INT32 accumulators)."""
+def _new_y(M, N, out, device):
     torch = _torch()
+    return torch.empty((M, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=device)
+
+
+def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False,
+           fmt: str = "s3d8", out: str = "f32"):
+    """Fused S3D8 (or 3D8) linear on pre-quantised activations: y [M][N],
+    fp32 or bf16 (and the INT32 accumulators)."""
+    torch = _torch()
+    f, o = _variant(fmt, out)
     _dev_check(xq, torch.int8, "xq")
     _dev_check(xs, torch.float32, "xs")
     scales = _scales_view(scales)
     M, K = xq.shape
-    _check_weights(tiled, centroids, scales, N, K)
+    _check_weights(tiled, centroids, scales, N, K, fmt)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+        y = _new_y(M, N, out, xq.device)
     if return_acc and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     with torch.cuda.device(xq.device):
-        call("s3d8_linear", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(),
-             centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
-             acc.data_ptr() if acc is not None else None, _stream(xq))
+        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr())
+        tail = (acc.data_ptr() if acc is not None else None, _stream(xq))
+        if f == 0 and o == 0:
+            call("s3d8_linear", *args, scales.data_ptr(), y.data_ptr(), *tail)
+        else:
+            call("s3d8_linear_ex", *args, f, scales.data_ptr(), y.data_ptr(), o, *tail)
     if return_acc:
         return y, acc
     return y
@@ -174,45 +208,50 @@ def unfused_workspace_bytes(N: int, K: int) -> int:
 
 
 def linear_unfused(xq, xs, tiled, centroids, scales, N: int, workspace=None, y=None, acc=None,
-                   return_acc: bool = False):
+                   return_acc: bool = False, fmt: str = "s3d8", out: str = "f32"):
     """Same result as ``linear``: the matrix is decoded once into an INT8
     workspace (allocated here unless given), then an INT8 GEMM runs on it."""
     torch = _torch()
+    f, o = _variant(fmt, out)
     _dev_check(xq, torch.int8, "xq")
     _dev_check(xs, torch.float32, "xs")
     scales = _scales_view(scales)
     M, K = xq.shape
-    _check_weights(tiled, centroids, scales, N, K)
+    _check_weights(tiled, centroids, scales, N, K, fmt)
     wbytes = unfused_workspace_bytes(N, K)
     if workspace is None:
         workspace = torch.empty((wbytes,), dtype=torch.int8, device=xq.device)
     _dev_check(workspace, torch.int8, "workspace")
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+        y = _new_y(M, N, out, xq.device)
     if return_acc and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
     with torch.cuda.device(xq.device):
-        call("s3d8_linear_unfused", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(),
-             centroids.data_ptr(), scales.data_ptr(), y.data_ptr(),
-             acc.data_ptr() if acc is not None else None, workspace.data_ptr(), workspace.numel(),
-             _stream(xq))
+        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr())
+        tail = (acc.data_ptr() if acc is not None else None, workspace.data_ptr(), workspace.numel(),
+                _stream(xq))
+        if f == 0 and o == 0:
+            call("s3d8_linear_unfused", *args, scales.data_ptr(), y.data_ptr(), *tail)
+        else:
+            call("s3d8_linear_unfused_ex", *args, f, scales.data_ptr(), y.data_ptr(), o, *tail)
     if return_acc:
         return y, acc
     return y
 
 
 def forward(x, tiled, centroids, scales, N: int, y=None, xq=None, xs=None, acc=None,
-            return_all: bool = False):
-    """The whole path from fp32 x [M][K]: quantise and apply the S3D8 linear
-    (one kernel launch for M <= 4).  Returns y, or (y, xq, xs, acc) with
-    ``return_all``."""
+            return_all: bool = False, fmt: str = "s3d8", out: str = "f32"):
+    """The whole path from fp32 x [M][K]: quantise and apply the S3D8 (or
+    3D8) linear (one kernel launch for M <= 4).  Returns y, or (y, xq, xs,
+    acc) with ``return_all``."""
     torch = _torch()
+    f, o = _variant(fmt, out)
     _dev_check(x, torch.float32, "x")
     scales = _scales_view(scales)
     M, K = x.shape
-    _check_weights(tiled, centroids, scales, N, K)
+    _check_weights(tiled, centroids, scales, N, K, fmt)
     if y is None:
-        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        y = _new_y(M, N, out, x.device)
     if xq is None:
         xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
     if xs is None:
@@ -220,9 +259,13 @@ def forward(x, tiled, centroids, scales, N: int, y=None, xq=None, xs=None, acc=N
     if return_all and acc is None:
         acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
     with torch.cuda.device(x.device):
-        call("s3d8_forward", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(),
-             scales.data_ptr(), y.data_ptr(), xq.data_ptr(), xs.data_ptr(),
-             acc.data_ptr() if acc is not None else None, _stream(x))
+        tail = (xq.data_ptr(), xs.data_ptr(), acc.data_ptr() if acc is not None else None, _stream(x))
+        if f == 0 and o == 0:
+            call("s3d8_forward", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(),
+                 scales.data_ptr(), y.data_ptr(), *tail)
+        else:
+            call("s3d8_forward_ex", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(), f,
+                 scales.data_ptr(), y.data_ptr(), o, *tail)
     if return_all:
         return y, xq, xs, acc
     return y
@@ -286,18 +329,23 @@ def encode_device(W, centroids):
     return scales, packed
 
 
-def dequant(packed, centroids, N: int, w=None):
+def dequant(packed, centroids, N: int, w=None, fmt: str = "s3d8"):
     """Standalone decode to channel-INT8: w int8 [N][K]."""
     torch = _torch()
+    f, _ = _variant(fmt)
     _dev_check(packed, torch.uint8, "packed")
-    _dev_check(centroids, torch.uint8, "centroids")
+    centroids = _table_view(centroids, fmt)
     T, K = packed.shape
     if T != num_triples(N):
         raise ValueError("packed rows do not match N")
     if w is None:
         w = torch.empty((N, K), dtype=torch.int8, device=packed.device)
     with torch.cuda.device(packed.device):
-        call("s3d8_dequant", packed.data_ptr(), centroids.data_ptr(), N, K, w.data_ptr(), _stream(packed))
+        if f == 0:
+            call("s3d8_dequant", packed.data_ptr(), centroids.data_ptr(), N, K, w.data_ptr(), _stream(packed))
+        else:
+            call("s3d8_dequant_ex", packed.data_ptr(), centroids.data_ptr(), f, N, K, w.data_ptr(),
+                 _stream(packed))
     return w
 
 

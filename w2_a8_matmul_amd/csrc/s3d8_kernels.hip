@@ -50,6 +50,16 @@ __device__ __forceinline__ uint32_t signed_triple(uint32_t b, const uint8_t *C) 
     return (uint32_t)(w0 & 0xFF) | ((uint32_t)(w1 & 0xFF) << 8) | ((uint32_t)(w2 & 0xFF) << 16);
 }
 
+// Row b of a 3D8 table as bytes [w0, w1, w2, 0].  3D8 is the unstructured
+// format the blog sets beside S3D8 ("S3D8: a 2.7-bit weight format for fast
+// decoding"): the whole byte indexes a (256, 3) table of signed values,
+// here int8, row-major, 768 bytes.  Channel packing, scales and layout are
+// those of S3D8, so both formats decode through the same 256-entry table.
+__device__ __forceinline__ uint32_t row_3d8(uint32_t b, const uint8_t *T) {
+    return (uint32_t)T[3 * b] | ((uint32_t)T[3 * b + 1] << 8) | ((uint32_t)T[3 * b + 2] << 16);
+}
+constexpr int kTableWords3D8 = 192;  // 768 bytes (the S3D8 table is 24 words)
+
 // Decode 16 packed bytes (k = 0..15 of one channel triple) into three
 // 16-byte INT8 vectors, one per channel of the triple: o_d byte k = w_d(k).
 __device__ __forceinline__ void decode16(const uint4 p, const uint32_t lane_off, const uint32_t *tab,
@@ -80,6 +90,11 @@ __device__ __forceinline__ void decode16(const uint4 p, const uint32_t lane_off,
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Round to nearest even of a finite fp32 to bfloat16 bits.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
 
 // Raw buffer loads (buffer_load_dwordx4): an offset at or past the buffer
 // size returns zeros without touching memory, so predicated-off lanes need no
@@ -122,23 +137,30 @@ __device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, v4i r
         : "memory");
 }
 
-// Stage the 96-byte centroid table (read through the scalar cache, so it does
-// not queue behind the vector loads already in flight) into LDS, then build
-// the lane-interleaved signed table.  C32 must be 4-byte aligned.  Contains
-// barriers.
-__device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *clw, const uint32_t *__restrict__ C32) {
-    uint32_t cw[24];
+// Stage the weight table into LDS (clw: kTableWords3D8 words), then build the
+// lane-interleaved signed table.  S3D8: the 96-byte centroid table, read
+// through the scalar cache so that it does not queue behind vector loads
+// already in flight; 3D8 (f3d8): the 768-byte signed table, one word per
+// thread.  C32 must be 4-byte aligned.  Contains barriers.
+__device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *clw, const uint32_t *__restrict__ C32,
+                                                      bool f3d8) {
+    if (f3d8) {
+        for (int i = threadIdx.x; i < kTableWords3D8; i += blockDim.x) clw[i] = C32[i];
+    } else {
+        uint32_t cw[24];
 #pragma unroll
-    for (int i = 0; i < 24; ++i) cw[i] = C32[i];
-    if (threadIdx.x == 0) {
+        for (int i = 0; i < 24; ++i) cw[i] = C32[i];
+        if (threadIdx.x == 0) {
 #pragma unroll
-        for (int i = 0; i < 6; ++i)
-            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+            for (int i = 0; i < 6; ++i)
+                reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+        }
     }
     __syncthreads();
     const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
     for (int idx = threadIdx.x; idx < kTabWords / 4; idx += blockDim.x) {
-        const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+        const uint32_t b = (uint32_t)idx >> 4;
+        const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
         reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
     }
     __syncthreads();
@@ -260,12 +282,12 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     const int8_t *__restrict__ xq, const float *__restrict__ xs, const float *__restrict__ xf,
     int8_t *__restrict__ xq_out, float *__restrict__ xs_out, int M, int K, int N, int T,
     const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, float *__restrict__ y, int32_t *__restrict__ acc_out,
-    int kbw) {
+    const uint16_t *__restrict__ scales, void *__restrict__ y, int32_t *__restrict__ acc_out,
+    int kbw, int f3d8, int obf) {
     constexpr int kThreads = WAVES * 64;
     __shared__ uint32_t tab[kTabWords];
     __shared__ int32_t red[16 * 48];
-    __shared__ uint32_t clw[24];
+    __shared__ uint32_t clw[kTableWords3D8];
     __shared__ float rmax[FUSED ? WAVES * kFusedMaxRows : 1];
     __shared__ float srow[FUSED ? kFusedMaxRows : 1];
     extern __shared__ int8_t xw[];  // FUSED: [WAVES][M][64 * kbw] INT8 codes, then 16 zero bytes
@@ -285,6 +307,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     uint32_t cw[24];
 #pragma unroll
     for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+    const uint32_t c3 = (f3d8 && tid < kTableWords3D8) ? centroids[tid] : 0u;  // 3D8: one word per thread
     // epilogue: output idx = tid + j * kThreads is (row idx / 48, channel
     // idx % 48 of the tile); its scales are fetched a tile ahead
     constexpr int kEp = (16 * 48 + kThreads - 1) / kThreads;
@@ -373,8 +396,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     int tile = blockIdx.x;
     if (tile < tiles) load(A, tile, 0);
 
-    // signed table from the centroid words loaded at the top
-    if (tid == 0) {
+    // signed table from the table words loaded at the top
+    if (f3d8) {
+        if (tid < kTableWords3D8) clw[tid] = c3;
+    } else if (tid == 0) {
 #pragma unroll
         for (int i = 0; i < 6; ++i)
             reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
@@ -383,7 +408,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
     {
         const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
         for (int idx = tid; idx < kTabWords / 4; idx += kThreads) {
-            const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+            const uint32_t b = (uint32_t)idx >> 4;
+            const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
             reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
         }
     }
@@ -489,7 +515,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
                 if (ch < N) {
                     const float sx = FUSED ? srow[r] : ep_sx[j];
                     const float v = (sx * (float)sum) * a_cur;
-                    y[(int64_t)r * N + ch] = v;
+                    if (obf)
+                        static_cast<uint16_t *>(y)[(int64_t)r * N + ch] = f32_to_bf16_rne(v);
+                    else
+                        static_cast<float *>(y)[(int64_t)r * N + ch] = v;
                     if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
                 }
             }
@@ -593,11 +622,12 @@ struct StreamBatch {
     StreamProb p[kStreamBatch];
 };
 
-template <int MR, int W, int NF>
+template <int MR, int W, int NF, bool F3>
 __device__ __forceinline__ void gemv_stream_body(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
     const uint16_t *__restrict__ scales, int K, int N, int bid, int grid, int ntw_q, int ntw_r,
-    float *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
+    void *__restrict__ y, int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out,
+    int obf) {
     static_assert(MR >= 1 && MR <= kFusedMaxRows, "1 to 4 token rows");
     const int T = (N + 2) / 3;
     const int kbw = (((K + 63) >> 6) + W - 1) / W;  // 64-column blocks per wave
@@ -644,19 +674,22 @@ __device__ __forceinline__ void gemv_stream_body(
         ep_a[q] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (idx < nout && ch < N) ? (uint32_t)ch * 2u : kOOB, 0, 0);
     }
 
-    // 2. the centroid rows of this thread's table entries: entry b = idx / 16
-    //    of uint4 idx = tid + kThreads i uses row (b / 2) % 32, which takes
-    //    kCenRows distinct values per thread (8 bytes from a 4-aligned
-    //    offset inside the 96-byte table each)
+    // 2. the table rows of this thread's table entries (8 bytes from a
+    //    4-aligned offset inside the table each).  S3D8: entry b = idx / 16
+    //    of uint4 idx = tid + kThreads i uses centroid row (b / 2) % 32,
+    //    which takes kCenRows distinct values per thread.  3D8 (F3): entry b
+    //    is row b of the 768-byte signed table, one row per pass.
     constexpr int kCenRows = 1024 / kThreads;
-    const v4i rcen = rsrc_words(centroids, 96u);
-    u2v cpair[kCenRows];
-    int cshift[kCenRows];
+    constexpr int kPasses = kTabWords / 4 / kThreads;
+    constexpr int kRows = F3 ? kPasses : kCenRows;
+    const v4i rcen = rsrc_words(centroids, F3 ? 768u : 96u);
+    u2v cpair[kRows];
+    int cshift[kRows];
 #pragma unroll
-    for (int k = 0; k < kCenRows; ++k) {
-        const int qrow = ((tid >> 5) + k * (kThreads >> 5)) & 31;
-        const int cbase = min((3 * qrow) & ~3, 88);
-        cshift[k] = 8 * (3 * qrow - cbase);
+    for (int k = 0; k < kRows; ++k) {
+        const int trow = F3 ? (tid >> 4) + k * (kThreads >> 4) : ((tid >> 5) + k * (kThreads >> 5)) & 31;
+        const int cbase = min((3 * trow) & ~3, F3 ? 760 : 88);
+        cshift[k] = 8 * (3 * trow - cbase);
         asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(cpair[k]) : "v"((uint32_t)cbase), "s"(rcen) : "memory");
     }
 
@@ -719,14 +752,18 @@ __device__ __forceinline__ void gemv_stream_body(
     // fixed, q takes kCenRows values and S1, bit 7 depend on i only: every
     // value is one of two low halves or-ed with one of two high halves of
     // its centroid row.
-    constexpr int kPasses = kTabWords / 4 / kThreads;
     static_assert(kCenRows * kThreads == 1024 && kPasses * kThreads == 4096, "table passes");
-    if constexpr (kCenRows == 1) {
-        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(cpair[0]) : "n"(kStreamSlots + NF) : "memory");
+    // (the empty statements after the wait keep every use of the rows behind it)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStreamSlots + NF) : "memory");
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) asm volatile("" : "+v"(cpair[k]));
+    if constexpr (F3) {
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            const uint32_t v = (uint32_t)((((uint64_t)cpair[i].y << 32) | cpair[i].x) >> cshift[i]) & 0xFFFFFFu;
+            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
+        }
     } else {
-        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(cpair[0]), "+v"(cpair[1]) : "n"(kStreamSlots + NF) : "memory");
-    }
-    {
         const bool s0 = (tid >> 4) & 1;
         uint32_t lo[kCenRows][2], hi[kCenRows][2];
 #pragma unroll
@@ -923,7 +960,11 @@ __device__ __forceinline__ void gemv_stream_body(
 #pragma unroll
             for (int rr = 1; rr < kFusedMaxRows; ++rr) sx = (r == rr) ? srow[rr] : sx;
             const int32_t sum = ybuf[(jj * kFusedMaxRows + r) * 48 + c];
-            y[(int64_t)r * N + ch] = (sx * (float)sum) * bf16_to_f32(ep_a[q]);
+            const float v = (sx * (float)sum) * bf16_to_f32(ep_a[q]);
+            if (obf)
+                static_cast<uint16_t *>(y)[(int64_t)r * N + ch] = f32_to_bf16_rne(v);
+            else
+                static_cast<float *>(y)[(int64_t)r * N + ch] = v;
             if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
         }
     }
@@ -948,13 +989,13 @@ __device__ __forceinline__ void gemv_stream_body(
 
 // One matrix: the arguments used before the first loads come first, so that
 // they are among the kernel arguments preloaded into SGPRs.
-template <int MR, int W, int NF>
+template <int MR, int W, int NF, bool F3>
 __global__ __launch_bounds__(W * 64) void gemv_stream_kernel(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
-    const uint16_t *__restrict__ scales, int K, int N, int grid, int ntw_q, int ntw_r, float *__restrict__ y,
-    int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out) {
-    gemv_stream_body<MR, W, NF>(xf, tiled, centroids, scales, K, N, (int)blockIdx.x, grid, ntw_q, ntw_r, y, acc_out,
-                                xq_out, xs_out);
+    const uint16_t *__restrict__ scales, int K, int N, int grid, int ntw_q, int ntw_r, void *__restrict__ y,
+    int32_t *__restrict__ acc_out, int8_t *__restrict__ xq_out, float *__restrict__ xs_out, int obf) {
+    gemv_stream_body<MR, W, NF, F3>(xf, tiled, centroids, scales, K, N, (int)blockIdx.x, grid, ntw_q, ntw_r, y,
+                                    acc_out, xq_out, xs_out, obf);
 }
 
 // Several matrices: this workgroup's matrix is the last p with wg0[p] <=
@@ -965,8 +1006,9 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamB
 #pragma unroll
     for (int q = 1; q < kStreamBatch; ++q) pi += (int)blockIdx.x >= B.wg0[q];
     const StreamProb &P = B.p[pi];
-    gemv_stream_body<MR, W, NF>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N, (int)blockIdx.x - B.wg0[pi],
-                            B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
+    gemv_stream_body<MR, W, NF, false>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N,
+                                       (int)blockIdx.x - B.wg0[pi], B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r,
+                                       P.y, P.acc_out, P.xq_out, P.xs_out, 0);
 }
 
 // --------------------------------------------------------------- GEMM
@@ -1064,10 +1106,14 @@ __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
 // triple straddles N (at most one per matrix) stores its valid channels one
 // by one instead, in a second pass only its wave runs.  Offsets stay below
 // 2^32: the caller keeps 128 rows of y under 2^31 bytes.
-template <bool kTriple, bool kAcc, int RT>
+//
+// kBF: y is bfloat16 (round to nearest even of the fp32 value, as the
+// blog's fused kernel writes its results); every channel goes out as its
+// own 2-byte store.
+template <bool kTriple, bool kAcc, int RT, bool kBF = false>
 __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const float *__restrict__ xs, int M,
                                                 int N, int row0, int h, const float (&sc)[3], const uint32_t (&coff)[3],
-                                                float *__restrict__ y, int32_t *__restrict__ acc_out) {
+                                                void *__restrict__ y, int32_t *__restrict__ acc_out) {
     const int nrows = min(M - row0, 32 * RT);
     const uint32_t rowb = 4u * (uint32_t)N;
     const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
@@ -1077,16 +1123,37 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
 #pragma unroll
         for (int g = 0; g < 4; ++g)
             sx[i][g] = __builtin_bit_cast(float4, bload16(rxs, 4u * (uint32_t)(32 * i + 8 * g + 4 * h)));
-    const auto ry = make_rsrc(y + (int64_t)row0 * N, rowb * (uint32_t)nrows);
     const auto ra = make_rsrc(acc_out + (int64_t)row0 * N, kAcc ? rowb * (uint32_t)nrows : 0u);
     uint32_t base[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) base[j] = coff[j] + (uint32_t)(4 * h) * rowb;
     // bit 31 when row 32 i + 8 (v / 4) + v % 4 + 4 h is past M
     auto dead = [&](int r) { return (uint32_t)(nrows - 1 - r - 4 * h) & kOOB; };
-    auto out = [&](int i, int v, int j) {
-        return __float_as_uint((sx[i][v >> 2][v & 3] * (float)acc[i][j][v]) * sc[j]);
-    };
+    auto outf = [&](int i, int v, int j) { return (sx[i][v >> 2][v & 3] * (float)acc[i][j][v]) * sc[j]; };
+    auto out = [&](int i, int v, int j) { return __float_as_uint(outf(i, v, j)); };
+    if constexpr (kBF) {
+        const uint32_t yrowb = 2u * (uint32_t)N;
+        const auto ry = make_rsrc(static_cast<uint16_t *>(y) + (int64_t)row0 * N, yrowb * (uint32_t)nrows);
+        uint32_t ybase[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) ybase[j] = (coff[j] == kOOB ? kOOB : coff[j] >> 1) + (uint32_t)(4 * h) * yrowb;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + (v & 3);
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(outf(i, v, j)), ry,
+                                                          (ybase[j] + (uint32_t)r * yrowb) | dead(r), 0, 0);
+                    if constexpr (kAcc)
+                        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra,
+                                                              (base[j] + (uint32_t)r * rowb) | dead(r), 0, 0);
+                }
+            }
+        return;
+    }
+    const auto ry = make_rsrc(static_cast<float *>(y) + (int64_t)row0 * N, rowb * (uint32_t)nrows);
     if constexpr (kTriple) {
         typedef uint32_t u3 __attribute__((ext_vector_type(3)));
         const bool split = coff[0] != kOOB && coff[2] == kOOB;
@@ -1132,12 +1199,12 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
     }
 }
 
-template <int RT, bool kAcc>
+template <int RT, bool kAcc, bool kBF>
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
                                                    const uint32_t *__restrict__ centroids,
-                                                   const uint16_t *__restrict__ scales, float *__restrict__ y,
-                                                   int32_t *__restrict__ acc_out, int nbm, int nbn) {
+                                                   const uint16_t *__restrict__ scales, void *__restrict__ y,
+                                                   int32_t *__restrict__ acc_out, int nbm, int nbn, int f3d8) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     constexpr int BM = 32 * RT;          // token rows per workgroup
     constexpr int NA = (2 * RT + 3) / 4;  // activation loads per wave and block
@@ -1145,7 +1212,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][BM * 64];
     __shared__ __attribute__((aligned(16))) int8_t spill[(4 * NA > 2 * RT) ? 1024 : 16];
     __shared__ __attribute__((aligned(16))) int8_t wbuf[kGemmSlots][kGemmBF * 1024];
-    __shared__ uint32_t clw[24];
+    __shared__ uint32_t clw[kTableWords3D8];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1159,9 +1226,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     const int row0 = bm * BM;
     const int frag0 = bn * kGemmBF + wave * 2;
 
+    // the table: S3D8's 96 bytes through the scalar cache; 3D8's 768 bytes as
+    // one word per thread (an explicit load, waited for below; an
+    // out-of-range offset reads nothing for S3D8)
     uint32_t cw[24];
 #pragma unroll
     for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+    uint32_t c3;
+    {
+        const v4i rc3 = rsrc_words(centroids, 768u);
+        const uint32_t off = (f3d8 && tid < kTableWords3D8) ? 4u * (uint32_t)tid : kOOB;
+        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(c3) : "v"(off), "s"(rc3) : "memory");
+    }
 
     const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
     const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
@@ -1239,7 +1315,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // prologue: blocks 0 .. kGemmAhead - 1 in flight, build the table
 #pragma unroll
     for (int s = 0; s < kGemmAhead; ++s) issue(s, s);
-    if (tid == 0) {
+    // (the table word is the oldest load: waiting until only the blocks'
+    // loads are in flight covers it)
+    asm volatile("s_waitcnt vmcnt(%1)" : "+v"(c3) : "n"(kGemmAhead * ND) : "memory");
+    if (f3d8) {
+        if (tid < kTableWords3D8) clw[tid] = c3;
+    } else if (tid == 0) {
 #pragma unroll
         for (int i = 0; i < 6; ++i)
             reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
@@ -1248,7 +1329,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     {
         const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
         for (int idx = tid; idx < kTabWords / 4; idx += 256) {
-            const uint32_t v = signed_triple((uint32_t)idx >> 4, cl);
+            const uint32_t b = (uint32_t)idx >> 4;
+            const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
             reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
         }
     }
@@ -1355,7 +1437,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
         coff[d] = ok ? 4u * (uint32_t)(ch0 + d) : kOOB;
         sc[d] = bf16_to_f32(bload2(rsc, ok ? 2u * (uint32_t)(ch0 + d) : kOOB));
     }
-    store_tile_rows<true, kAcc>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+    store_tile_rows<true, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- dequant
@@ -1366,10 +1448,10 @@ constexpr int kDequantThreads = 512;
 
 __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
     const uint8_t *__restrict__ packed, const uint32_t *__restrict__ centroids, int K, int N,
-    int64_t nchunks, int8_t *__restrict__ w) {
+    int64_t nchunks, int8_t *__restrict__ w, int f3d8) {
     __shared__ uint32_t tab[kTabWords];
-    __shared__ uint32_t clw[24];
-    stage_and_build_table(tab, clw, centroids);
+    __shared__ uint32_t clw[kTableWords3D8];
+    stage_and_build_table(tab, clw, centroids, f3d8 != 0);
     const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
     const int cpr = K >> 4;  // 16-byte chunks per triple row
     for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
@@ -1404,10 +1486,10 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
 // c / 64, lane c % 64 = triple n + 16 g of the fragment, columns 16 g ..
 __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
     const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids, int K, int T, int KB,
-    int64_t nchunks, int8_t *__restrict__ w8) {
+    int64_t nchunks, int8_t *__restrict__ w8, int f3d8) {
     __shared__ uint32_t tab[kTabWords];
-    __shared__ uint32_t clw[24];
-    stage_and_build_table(tab, clw, centroids);
+    __shared__ uint32_t clw[kTableWords3D8];
+    stage_and_build_table(tab, clw, centroids, f3d8 != 0);
     const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
     for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
          c += (int64_t)gridDim.x * kDequantThreads) {
@@ -1442,10 +1524,10 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
 constexpr int kI8Slots = 5;
 constexpr int kI8Ahead = kI8Slots - 1;
 
-template <bool kAcc>
+template <bool kAcc, bool kBF>
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       int M, int K, int N, int NP, const int8_t *__restrict__ w8,
-                                                      const uint16_t *__restrict__ scales, float *__restrict__ y,
+                                                      const uint16_t *__restrict__ scales, void *__restrict__ y,
                                                       int32_t *__restrict__ acc_out, int nbm, int nbn) {
     __shared__ __attribute__((aligned(16))) int8_t abuf[kI8Slots][kGemmBM * 64];
     __shared__ __attribute__((aligned(16))) int8_t bbuf[kI8Slots][4 * 6 * 1024];
@@ -1584,7 +1666,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         coff[ct] = ch < N ? 4u * (uint32_t)ch : kOOB;
         sc[ct] = bf16_to_f32(bload2(rsc, ch < N ? 2u * (uint32_t)ch : kOOB));
     }
-    store_tile_rows<false, kAcc>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+    store_tile_rows<false, kAcc, kGemmRT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- encode on the device
@@ -1616,7 +1698,7 @@ __global__ __launch_bounds__(kScaleThreads) void channel_scale_kernel(const floa
         const float s = m / 127.0f;  // IEEE division
         const uint32_t u = __float_as_uint(s);
         // round to nearest even on the upper 16 bits (s is finite and >= 0)
-        alpha[i] = (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        alpha[i] = f32_to_bf16_rne(__uint_as_float(u));
     }
 }
 
@@ -1719,8 +1801,9 @@ struct GemvArgs {
     const uint8_t *tiled;
     const uint32_t *centroids;
     const uint16_t *scales;
-    float *y;
+    void *y;
     int32_t *acc_out;
+    int f3d8, obf;  // 3D8 table; bf16 output
 };
 
 // kbw = 64-column blocks per wave; the fused prologue needs M * kbw <= 16
@@ -1741,7 +1824,7 @@ bool launch_gemv(GemvConfig cfg, bool fused, const GemvArgs &a, int cus, hipStre
     if (cfg.waves == W && cfg.unroll == U && fused == F) {                                               \
         hipLaunchKernelGGL((gemv_kernel<W, U, F>), dim3(grid), dim3(W * 64), xw_bytes, stream, a.xq, a.xs, \
                            a.xf, a.xq_out, a.xs_out, a.M, a.K, a.N, a.T, a.tiled, a.centroids, a.scales,  \
-                           a.y, a.acc_out, kbw);                                                         \
+                           a.y, a.acc_out, kbw, a.f3d8, a.obf);                                          \
         return true;                                                                                     \
     }
     S3D8_GEMV_CASE(16, 2, false)
@@ -1783,9 +1866,12 @@ bool stream_split(int count, const int64_t *tiles, const int64_t *K, int cus, in
 }
 
 // One launch of gemv_stream_kernel over `count` matrices that share M; false
-// (nothing launched) if a matrix does not fit the kernel.
-bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus, hipStream_t stream) {
+// (nothing launched) if a matrix does not fit the kernel.  A single matrix
+// may be 3D8 (f3d8) and write bf16 (obf); a batch is S3D8 with fp32 output.
+bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus, hipStream_t stream,
+                              bool f3d8 = false, int obf = 0) {
     if (count < 1 || count > kStreamBatch) return false;
+    if (count > 1 && (f3d8 || obf)) return false;
     const int64_t M = items[0].M;
     if (M < 1 || M > kFusedMaxRows) return false;
     // 16 waves (8 were measured slower at K = 4096: the shorter prologue is
@@ -1819,11 +1905,13 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     int NF = 1;
     for (int p = 0; p < count; ++p) NF = std::max(NF, (int)((M * B.p[p].kbw + 3) / 4));
     typedef void (*Single)(const float *, const uint8_t *, const uint8_t *, const uint16_t *, int, int, int, int, int,
-                           float *, int32_t *, int8_t *, float *);
+                           void *, int32_t *, int8_t *, float *, int);
     typedef void (*Batched)(StreamBatch);
-#define S3D8_ROW(m) {gemv_stream_kernel<m, W, 1>, gemv_stream_kernel<m, W, 2>, gemv_stream_kernel<m, W, 3>, \
-                      gemv_stream_kernel<m, W, 4>}
-    static const Single single[4][4] = {S3D8_ROW(1), S3D8_ROW(2), S3D8_ROW(3), S3D8_ROW(4)};
+#define S3D8_ROW(m, f) {gemv_stream_kernel<m, W, 1, f>, gemv_stream_kernel<m, W, 2, f>, \
+                         gemv_stream_kernel<m, W, 3, f>, gemv_stream_kernel<m, W, 4, f>}
+    static const Single single[2][4][4] = {
+        {S3D8_ROW(1, false), S3D8_ROW(2, false), S3D8_ROW(3, false), S3D8_ROW(4, false)},
+        {S3D8_ROW(1, true), S3D8_ROW(2, true), S3D8_ROW(3, true), S3D8_ROW(4, true)}};
 #undef S3D8_ROW
 #define S3D8_ROW(m) {gemv_stream_batch_kernel<m, W, 1>, gemv_stream_batch_kernel<m, W, 2>, \
                       gemv_stream_batch_kernel<m, W, 3>, gemv_stream_batch_kernel<m, W, 4>}
@@ -1831,8 +1919,9 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
 #undef S3D8_ROW
     if (count == 1) {
         const StreamProb &P = B.p[0];
-        hipLaunchKernelGGL(single[M - 1][NF - 1], dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf, P.tiled,
-                           P.centroids, P.scales, P.K, P.N, wg, P.ntw_q, P.ntw_r, P.y, P.acc_out, P.xq_out, P.xs_out);
+        hipLaunchKernelGGL(single[f3d8 ? 1 : 0][M - 1][NF - 1], dim3((unsigned)wg), dim3(W * 64), 0, stream, P.xf,
+                           P.tiled, P.centroids, P.scales, P.K, P.N, wg, P.ntw_q, P.ntw_r, (void *)P.y, P.acc_out,
+                           P.xq_out, P.xs_out, obf);
         return true;
     }
     auto kern = batched[M - 1][NF - 1];
@@ -1841,10 +1930,11 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
 }
 
 bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_t K, int64_t N,
-                        const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, float *y,
-                        int32_t *acc_out, int cus, hipStream_t stream) {
-    const s3d8_forward_item it{x, M, K, N, tiled, centroids, scales, y, xq, xs, acc_out};
-    return launch_gemv_stream_batch(1, &it, cus, stream);
+                        const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, void *y,
+                        int32_t *acc_out, int cus, hipStream_t stream, bool f3d8, int obf) {
+    // (the item's y is only passed on: the kernel stores through it as bf16 when obf)
+    const s3d8_forward_item it{x, M, K, N, tiled, centroids, scales, static_cast<float *>(y), xq, xs, acc_out};
+    return launch_gemv_stream_batch(1, &it, cus, stream, f3d8, obf);
 }
 
 }  // namespace
@@ -1889,29 +1979,37 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
 }
 
 namespace {
-int check_linear_args(const void *tiled, const uint8_t *centroids, const uint16_t *scales, const float *y,
-                      int64_t M, int64_t K, int64_t N) {
-    if (!tiled || !centroids || !scales || !y) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+int check_linear_args(const void *tiled, const void *table, const uint16_t *scales, const void *y, int64_t M,
+                      int64_t K, int64_t N) {
+    if (!tiled || !table || !scales || !y) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
     int rc = check_sizes(M, K, N);
     if (rc) return rc;
     if (tiled_bytes(N, K) > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "tiled weights over 2^31 bytes");
     if (!aligned16(tiled)) return s3d8::fail(S3D8_ERR_ALIGN, "tiled weights must be 16-byte aligned");
-    if (reinterpret_cast<uintptr_t>(centroids) & 3u)
-        return s3d8::fail(S3D8_ERR_ALIGN, "centroids must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(table) & 3u)
+        return s3d8::fail(S3D8_ERR_ALIGN, "the centroid table must be 4-byte aligned");
     return S3D8_OK;
 }
-}  // namespace
 
-int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
-                    float *y, int32_t *acc_out, void *stream) {
+int check_variant(int32_t format, int32_t out_type) {
+    if (format != S3D8_FORMAT_S3D8 && format != S3D8_FORMAT_3D8)
+        return s3d8::fail(S3D8_ERR_INVALID_ARG, "unknown weight format");
+    if (out_type != S3D8_OUT_F32 && out_type != S3D8_OUT_BF16)
+        return s3d8::fail(S3D8_ERR_INVALID_ARG, "unknown output type");
+    return S3D8_OK;
+}
+
+int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int32_t *acc_out,
+                void *stream) {
     if (!xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "xq must be 16-byte aligned");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
+    const uint32_t *table32 = reinterpret_cast<const uint32_t *>(table);
     if (M > 16) {
         if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
         const int64_t T = (N + 2) / 3;
@@ -1927,47 +2025,86 @@ int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int
         const int64_t nwg = (int64_t)nbm * nbn;
         const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
         if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-        auto kern = rt == 5 ? (acc_out ? gemm_kernel<5, true> : gemm_kernel<5, false>)
-                            : (acc_out ? gemm_kernel<4, true> : gemm_kernel<4, false>);
-        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K, (int)N,
-                           (int)T, tiled, reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y, acc_out, nbm,
-                           nbn);
+        typedef void (*GemmFn)(const int8_t *, const float *, int, int, int, int, const uint8_t *, const uint32_t *,
+                               const uint16_t *, void *, int32_t *, int, int, int);
+        static const GemmFn fns[2][2][2] = {
+            {{gemm_kernel<4, false, false>, gemm_kernel<4, false, true>},
+             {gemm_kernel<4, true, false>, gemm_kernel<4, true, true>}},
+            {{gemm_kernel<5, false, false>, gemm_kernel<5, false, true>},
+             {gemm_kernel<5, true, false>, gemm_kernel<5, true, true>}}};
+        hipLaunchKernelGGL(fns[rt == 5][acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0,
+                           (hipStream_t)stream, xq, xs, (int)M, (int)K, (int)N, (int)T, tiled, table32, scales_bf16, y,
+                           acc_out, nbm, nbn, (int)f3d8);
         return launch_status();
     }
     // the GEMV takes up to 16 token rows per launch
+    const size_t ysize = obf ? 2 : 4;
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
         const int mrows = (int)(M - m0 < 16 ? M - m0 : 16);
         GemvArgs a{xq + m0 * K, xs + m0, nullptr, nullptr, nullptr, mrows, (int)K, (int)N, (int)((N + 2) / 3),
-                   tiled, reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y + m0 * N,
-                   acc_out ? acc_out + m0 * N : nullptr};
+                   tiled, table32, scales_bf16, static_cast<char *>(y) + m0 * N * ysize,
+                   acc_out ? acc_out + m0 * N : nullptr, (int)f3d8, (int)obf};
         if (!launch_gemv(kGemvDefault, false, a, cus, (hipStream_t)stream))
             return s3d8::fail(S3D8_ERR_INVALID_ARG, "no GEMV variant for this launch shape");
     }
     return launch_status();
 }
 
-int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                     const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq, float *xs,
-                     int32_t *acc_out, void *stream) {
+int forward_impl(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
+                 bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int8_t *xq, float *xs,
+                 int32_t *acc_out, void *stream) {
     if (!x || !xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(x) || !aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "x and xq must be 16-byte aligned");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
-    if (launch_gemv_stream(x, xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, cus, (hipStream_t)stream))
+    const uint8_t *table8 = static_cast<const uint8_t *>(table);
+    if (launch_gemv_stream(x, xq, xs, M, K, N, tiled, table8, scales_bf16, y, acc_out, cus, (hipStream_t)stream,
+                           f3d8, (int)obf))
         return launch_status();
     if (gemv_fusable((int)M, (int)K, kGemvDefault)) {
         GemvArgs a{nullptr, nullptr, x, xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled,
-                   reinterpret_cast<const uint32_t *>(centroids), scales_bf16, y, acc_out};
+                   reinterpret_cast<const uint32_t *>(table), scales_bf16, y, acc_out, (int)f3d8, (int)obf};
         if (!launch_gemv(kGemvDefault, true, a, cus, (hipStream_t)stream))
             return s3d8::fail(S3D8_ERR_INVALID_ARG, "no fused GEMV variant for this launch shape");
         return launch_status();
     }
     rc = s3d8_quant_act(x, M, K, xq, xs, stream);
     if (rc) return rc;
-    return s3d8_linear(xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out, stream);
+    return linear_impl(xq, xs, M, K, N, tiled, table, f3d8, scales_bf16, y, obf, acc_out, stream);
+}
+}  // namespace
+
+int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
+                    float *y, int32_t *acc_out, void *stream) {
+    return linear_impl(xq, xs, M, K, N, tiled, centroids, false, scales_bf16, y, false, acc_out, stream);
+}
+
+int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                       const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
+                       int32_t *acc_out, void *stream) {
+    int rc = check_variant(format, out_type);
+    if (rc) return rc;
+    return linear_impl(xq, xs, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+                       out_type == S3D8_OUT_BF16, acc_out, stream);
+}
+
+int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                     const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq, float *xs,
+                     int32_t *acc_out, void *stream) {
+    return forward_impl(x, M, K, N, tiled, centroids, false, scales_bf16, y, false, xq, xs, acc_out, stream);
+}
+
+int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
+                        int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type, int8_t *xq, float *xs,
+                        int32_t *acc_out, void *stream) {
+    int rc = check_variant(format, out_type);
+    if (rc) return rc;
+    return forward_impl(x, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+                        out_type == S3D8_OUT_BF16, xq, xs, acc_out, stream);
 }
 
 int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *stream) {
@@ -2019,11 +2156,12 @@ int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
     return (3 * ((N + 2) / 3) + 31) / 32 * ((K + 63) / 64) * 2048;
 }
 
-int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16, float *y,
-                            int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
+namespace {
+int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                 const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int32_t *acc_out,
+                 int8_t *workspace, int64_t workspace_bytes, void *stream) {
     if (!xq || !xs || !workspace) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, centroids, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(xq) || !aligned16(workspace))
         return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
@@ -2040,25 +2178,30 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
     int64_t blocks = (nchunks + kDequantThreads - 1) / kDequantThreads;
     if (blocks > (int64_t)cus * 2) blocks = (int64_t)cus * 2;
     hipLaunchKernelGGL(dequant_tiled_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0, (hipStream_t)stream,
-                       tiled, reinterpret_cast<const uint32_t *>(centroids), (int)K, (int)T, KB, nchunks, workspace);
+                       tiled, reinterpret_cast<const uint32_t *>(table), (int)K, (int)T, KB, nchunks, workspace,
+                       (int)f3d8);
     const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
     const int nbn = (int)((3 * T + 383) / 384);
     const int64_t nwg = (int64_t)nbm * nbn;
     const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
     if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-    hipLaunchKernelGGL(acc_out ? gemm_i8_kernel<true> : gemm_i8_kernel<false>, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs, (int)M, (int)K,
-                       (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
+    typedef void (*I8Fn)(const int8_t *, const float *, int, int, int, int, const int8_t *, const uint16_t *, void *,
+                         int32_t *, int, int);
+    static const I8Fn fns[2][2] = {{gemm_i8_kernel<false, false>, gemm_i8_kernel<false, true>},
+                                   {gemm_i8_kernel<true, false>, gemm_i8_kernel<true, true>}};
+    hipLaunchKernelGGL(fns[acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs,
+                       (int)M, (int)K, (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
     return launch_status();
 }
 
-int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K, int8_t *w,
-                     void *stream) {
-    if (!packed || !centroids || !w) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+int dequant_impl(const uint8_t *packed, const void *table, bool f3d8, int64_t N, int64_t K, int8_t *w,
+                 void *stream) {
+    if (!packed || !table || !w) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
     int rc = check_sizes(1, K, N);
     if (rc) return rc;
     if (!aligned16(packed) || !aligned16(w)) return s3d8::fail(S3D8_ERR_ALIGN, "packed and w must be 16-byte aligned");
-    if (reinterpret_cast<uintptr_t>(centroids) & 3u)
-        return s3d8::fail(S3D8_ERR_ALIGN, "centroids must be 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(table) & 3u)
+        return s3d8::fail(S3D8_ERR_ALIGN, "the centroid table must be 4-byte aligned");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
@@ -2067,10 +2210,39 @@ int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N,
     int64_t blocks = (nchunks + kDequantThreads - 1) / kDequantThreads;
     const int64_t cap = (int64_t)cus * 2;
     if (blocks > cap) blocks = cap;
-    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0,
-                       (hipStream_t)stream, packed, reinterpret_cast<const uint32_t *>(centroids), (int)K,
-                       (int)N, nchunks, w);
+    hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0, (hipStream_t)stream, packed,
+                       reinterpret_cast<const uint32_t *>(table), (int)K, (int)N, nchunks, w, (int)f3d8);
     return launch_status();
+}
+}  // namespace
+
+int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16, float *y,
+                            int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
+    return unfused_impl(xq, xs, M, K, N, tiled, centroids, false, scales_bf16, y, false, acc_out, workspace,
+                        workspace_bytes, stream);
+}
+
+int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                               const uint8_t *tiled, const void *table, int32_t format, const uint16_t *scales_bf16,
+                               void *y, int32_t out_type, int32_t *acc_out, int8_t *workspace,
+                               int64_t workspace_bytes, void *stream) {
+    int rc = check_variant(format, out_type);
+    if (rc) return rc;
+    return unfused_impl(xq, xs, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+                        out_type == S3D8_OUT_BF16, acc_out, workspace, workspace_bytes, stream);
+}
+
+int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K, int8_t *w,
+                     void *stream) {
+    return dequant_impl(packed, centroids, false, N, K, w, stream);
+}
+
+int32_t s3d8_dequant_ex(const uint8_t *packed, const void *table, int32_t format, int64_t N, int64_t K, int8_t *w,
+                        void *stream) {
+    int rc = check_variant(format, S3D8_OUT_F32);
+    if (rc) return rc;
+    return dequant_impl(packed, table, format == S3D8_FORMAT_3D8, N, K, w, stream);
 }
 
 }  // extern "C"
