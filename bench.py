@@ -189,6 +189,25 @@ def main():
     qa_mean_us = graph_launch_us(torch, [lambda r=r: s3d8.quant_act(dX[r], xq, xsc) for r in range(R)], 10)
     log(f"step {ms_per_step * 1e3:.2f} us -> {value:.1f} GB/s; forward kernel {lin_mean_us:.2f} us "
         f"-> {achieved:.1f} GB/s; quant_act alone {qa_mean_us:.2f} us")
+
+    # ---------------------------------------------------------------- format and output variants
+    # the same decode step with 3D8 weights (a random int8 [256][3] signed
+    # table over the same bytes) and with bf16 outputs; effective bytes of
+    # 3D8 count its 768-byte table
+    T3d = torch.from_numpy(workloads.signed_table([7, 1])).to(dev)
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    variants = {"decode": {"workload": f"{lin.name}: M={M} K={K} N={N}"}}
+    for tag, tab, fmt, yy in (("s3d8_f32", dC, "s3d8", y), ("3d8_f32", T3d, "3d8", y),
+                              ("s3d8_bf16", dC, "s3d8", yb), ("3d8_bf16", T3d, "3d8", yb)):
+        out = "bf16" if yy is yb else "f32"
+        fns = [lambda r=r, tab=tab, fmt=fmt, yy=yy, out=out: s3d8.forward(dX[r], dP[r], tab, dS, N, y=yy, xq=xq,
+                                                                           xs=xsc, fmt=fmt, out=out)
+               for r in range(R)]
+        fns[0]()
+        v_us = graph_launch_us(torch, fns, 10)
+        vbytes = weight_bytes + (768 - 96 if fmt == "3d8" else 0)
+        variants["decode"][tag] = {"us": round(v_us, 3), "GBs": round(vbytes / (v_us * 1e-6) / 1e9, 1)}
+        log(f"variant {tag}: {v_us:.2f} us -> {variants['decode'][tag]['GBs']} GB/s effective weight bytes")
     del dP, dX
 
     # ---------------------------------------------------------------- one decoder-layer step (c2)
@@ -312,6 +331,20 @@ def main():
                     for r in range(Rp)], 5)
         u_tops = ops / (u_mean_us * 1e-6) / 1e12
         log(f"prefill GEMM {lp.name}: unfused (dequant + INT8 GEMM) {u_mean_us:.1f} us -> {u_tops:.1f} TOPS")
+        # format and output variants of the fused GEMM
+        T3p = torch.from_numpy(workloads.signed_table([7, 3])).to(dev)
+        ypb = torch.empty((lp.M, lp.N), dtype=torch.bfloat16, device=dev)
+        variants["prefill"] = {"workload": f"{lp.name}: M={lp.M} K={lp.K} N={lp.N}"}
+        for tag, tab, fmt, yy in (("3d8_f32", T3p, "3d8", yp), ("s3d8_bf16", dCp, "s3d8", ypb),
+                                  ("3d8_bf16", T3p, "3d8", ypb)):
+            out = "bf16" if yy is ypb else "f32"
+            fns = [lambda r=r, tab=tab, fmt=fmt, yy=yy, out=out: s3d8.linear(xqp, xsp, dPp[r], tab, dSp, lp.N, y=yy,
+                                                                              fmt=fmt, out=out)
+                   for r in range(Rp)]
+            fns[0]()
+            v_us = graph_launch_us(torch, fns, 5)
+            variants["prefill"][tag] = {"us": round(v_us, 2), "TOPS": round(ops / (v_us * 1e-6) / 1e12, 1)}
+            log(f"variant prefill {tag}: {v_us:.1f} us -> {variants['prefill'][tag]['TOPS']} TOPS")
         prefill = {
             "workload": f"{lp.name}: M={lp.M} K={lp.K} N={lp.N}",
             "value": round(tops, 2), "unit": "INT8 TOPS", "us_per_launch": round(g_mean_us, 2),
@@ -378,6 +411,7 @@ def main():
         "decoder_layer": layer,
         "encode": encode,
         "dequant": dequant,
+        "variants": variants,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
