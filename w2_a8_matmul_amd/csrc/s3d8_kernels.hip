@@ -725,7 +725,7 @@ __device__ __forceinline__ void gemv_stream_body(
     //    this wave = tile j = s / kbw of the workgroup, block kb0 + s % kbw,
     //    kStreamSlots steps in flight in a ring of registers; steps past the
     //    end read zeros (out-of-range offsets)
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
+    const v4i rw = rsrc_words(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
     int is_j = 0, is_b = 0;  // (tile, block) of the next step to issue
     auto next_off = [&]() {
         const int kb = kb0 + is_b;
@@ -738,9 +738,22 @@ __device__ __forceinline__ void gemv_stream_body(
         }
         return off;
     };
-    uint4 pr[kStreamSlots];
+    // The ring loads are issued from inline assembly and waited for
+    // explicitly (the compiler's own count at the loop header is not exact:
+    // it waits for every load in flight there).  Each load's destination is
+    // tied to its ring entry ("+v"), so no copy of an entry can be read
+    // before the load lands; every entry is waited for with vmcnt(slots - 1)
+    // before use: the younger loads in flight are the other entries.
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v pr[kStreamSlots];
+    auto ring_load = [&](u4v &dst, uint32_t off) {
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(dst) : "v"(off), "s"(rw) : "memory");
+    };
 #pragma unroll
-    for (int sl = 0; sl < kStreamSlots; ++sl) pr[sl] = bload16(rw, next_off());
+    for (int sl = 0; sl < kStreamSlots; ++sl) {
+        asm volatile("" : "=v"(pr[sl]));  // defined, with no code: the load below overwrites it
+        ring_load(pr[sl], next_off());
+    }
 
     for (int i = tid; i < ntw * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
@@ -914,7 +927,8 @@ __device__ __forceinline__ void gemv_stream_body(
 #pragma unroll
         for (int u = 0; u < kStreamSlots; ++u) {
             if (st0 + u >= nsteps) break;  // uniform
-            const uint4 p = pr[u];
+            asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pr[u]) : "n"(kStreamSlots - 1) : "memory");
+            const u4v p = pr[u];
             v4i a = {0, 0, 0, 0};
             if (arow) a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);  // 3M of 16 rows in use
             const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
@@ -931,7 +945,7 @@ __device__ __forceinline__ void gemv_stream_body(
             }
             // refill the entry once its bytes are consumed (so the new load
             // writes the same registers and the loop carries no copies)
-            pr[u] = bload16(rw, next_off());
+            ring_load(pr[u], next_off());
             if (++bl == kbw) {
                 // tile j done for this wave: lane (n, g) holds rows 4 g + i,
                 // row m = 3r + d is channel 3n + d of token r within the tile
