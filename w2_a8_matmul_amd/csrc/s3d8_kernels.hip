@@ -749,8 +749,12 @@ __device__ __forceinline__ void gemv_stream_body(
     auto ring_load = [&](u4v &dst, uint32_t off) {
         asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(dst) : "v"(off), "s"(rw) : "memory");
     };
+    // the first kEarly entries now, the rest after the workgroup barrier
+    // below: a wave stalled issuing weight loads behind the memory
+    // system's backlog reaches its absmax late and holds up the barrier
+    constexpr int kEarly = 2;
 #pragma unroll
-    for (int sl = 0; sl < kStreamSlots; ++sl) {
+    for (int sl = 0; sl < kEarly; ++sl) {
         asm volatile("" : "=v"(pr[sl]));  // defined, with no code: the load below overwrites it
         ring_load(pr[sl], next_off());
     }
@@ -767,7 +771,7 @@ __device__ __forceinline__ void gemv_stream_body(
     // its centroid row.
     static_assert(kCenRows * kThreads == 1024 && kPasses * kThreads == 4096, "table passes");
     // (the empty statements after the wait keep every use of the rows behind it)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStreamSlots + NF) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly + NF) : "memory");
 #pragma unroll
     for (int k = 0; k < kRows; ++k) asm volatile("" : "+v"(cpair[k]));
     if constexpr (F3) {
@@ -801,13 +805,13 @@ __device__ __forceinline__ void gemv_stream_body(
 
     // activations landed (only fragment loads behind them)
     if constexpr (NF == 1) {
-        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(xv[0]) : "n"(kStreamSlots) : "memory");
+        asm volatile("s_waitcnt vmcnt(%1)" : "+v"(xv[0]) : "n"(kEarly) : "memory");
     } else if constexpr (NF == 2) {
-        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(xv[0]), "+v"(xv[1]) : "n"(kStreamSlots) : "memory");
+        asm volatile("s_waitcnt vmcnt(%2)" : "+v"(xv[0]), "+v"(xv[1]) : "n"(kEarly) : "memory");
     } else if constexpr (NF == 3) {
-        asm volatile("s_waitcnt vmcnt(%3)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]) : "n"(kStreamSlots) : "memory");
+        asm volatile("s_waitcnt vmcnt(%3)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]) : "n"(kEarly) : "memory");
     } else {
-        asm volatile("s_waitcnt vmcnt(%4)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]) : "n"(kStreamSlots)
+        asm volatile("s_waitcnt vmcnt(%4)" : "+v"(xv[0]), "+v"(xv[1]), "+v"(xv[2]), "+v"(xv[3]) : "n"(kEarly)
                      : "memory");
     }
     // (16 waves share a CU's four SIMDs: every VALU operation here costs
@@ -828,6 +832,11 @@ __device__ __forceinline__ void gemv_stream_body(
         if (lane == 0) rmax[wave * kFusedMaxRows + r] = a;
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // table, rmax, ybuf complete
+#pragma unroll
+    for (int sl = kEarly; sl < kStreamSlots; ++sl) {
+        asm volatile("" : "=v"(pr[sl]));
+        ring_load(pr[sl], next_off());
+    }
 
     // per-token scale s = a / 127 (lane w of each row reads wave w's maximum),
     // codes clamp(rne(x / s), -127, 127) into this wave's slice of xw
