@@ -575,23 +575,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 // accumulators, xq and xs) happens after the last weight load has landed.
 constexpr int kStreamMaxTiles = 16;  // tiles per workgroup (results held in LDS)
 
+// Maxima of non-negative floats (absolute values and their maxima, never
+// NaN): for x >= +0 the IEEE bit patterns order like the values, so the
+// reductions compare them as unsigned integers (0 is the identity, and the
+// DPP moves fold into the max instructions).
 // max over each row of 16 lanes, result in every lane of the row (DPP:
 // swap neighbours, swap pairs, mirror halves of 8, mirror the row)
 __device__ __forceinline__ float row16_max(float v) {
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
-    return v;
+    uint32_t u = __float_as_uint(v);
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0xB1, 0xF, 0xF, false));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x4E, 0xF, 0xF, false));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x141, 0xF, 0xF, false));
+    u = max(u, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x140, 0xF, 0xF, false));
+    return __uint_as_float(u);
 }
 // max over the wave, wave-uniform
 __device__ __forceinline__ float wave_max(float v) {
-    v = row16_max(v);
-    const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
-    const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
-                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
-    return fmaxf(a, b);
+    const uint32_t u = __float_as_uint(row16_max(v));
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)u, 0), (uint32_t)__builtin_amdgcn_readlane((int)u, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)u, 32), (uint32_t)__builtin_amdgcn_readlane((int)u, 48));
+    return __uint_as_float(max(a, b));
 }
 
 // One launch can serve up to kStreamBatch independent matrices (e.g. the
@@ -759,6 +762,21 @@ __device__ __forceinline__ void gemv_stream_body(
         ring_load(pr[sl], next_off());
     }
 
+    // lane constants of the products' A operand (described with the loop
+    // below), computed here while the loads are in flight rather than after
+    // the barrier, where every wave of the CU is busy quantising
+    const int arw = lane & 15;
+    const bool arow = arw < 3 * M;
+    const int8_t *xa = arow ? &xw[wave][(arw / 3) * 64 * kbw + g * 16] : zero16;
+    const int xa_step = arow ? 64 : 0;
+    uint32_t asel[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t dpos = 8u * (uint32_t)(arw % 3);
+        asel[i] = (0x0C0C0C0Cu & ~(0xFFu << dpos)) | ((uint32_t)i << dpos);
+    }
+    asm volatile("" ::"v"(asel[0]), "v"(asel[1]), "v"(asel[2]), "v"(asel[3]), "v"(xa), "v"(xa_step));
+
     for (int i = tid; i < ntw * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
 
@@ -852,15 +870,16 @@ __device__ __forceinline__ void gemv_stream_body(
     // below 1 ulp): |t - x / s| < 2.5e-7 |x / s| <= 3.2e-5, so whenever t is
     // more than 1e-4 away from a half-integer, t, the exact quotient and its
     // fp32 rounding lie in the same rounding interval and rint(t) is the
-    // code.  Elements closer to a half-integer (and every element of a row
-    // whose s is below 1e-30) take the IEEE quotient instead, in a pass the
-    // wave runs only when one of its lanes needs it.
+    // code.  A lane with an element within 2e-4 of a half-integer (|t -
+    // rint(t)| >= 0.4998), or of a row whose s is below 1e-30, takes the
+    // IEEE quotient for all its elements instead, in a pass the wave runs
+    // only when one of its lanes needs it.
     float rcp[kFusedMaxRows] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int r = 0; r < M; ++r) rcp[r] = srow[r] >= 1e-30f ? __builtin_amdgcn_rcpf(srow[r]) : 0.0f;
     float qv[NF][4];
     float scv[NF];
-    uint32_t exact = 0;  // bit 4 i + e: element e of float4 i needs the quotient
+    bool slow = false;
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
         scv[i] = 0.0f;
@@ -873,23 +892,23 @@ __device__ __forceinline__ void gemv_stream_body(
             }
             scv[i] = sc;
             const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
-            const bool tiny = rc == 0.0f && sc != 0.0f;
+            slow = slow || (rc == 0.0f && sc != 0.0f);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float t = xe[e] * rc;
                 qv[i][e] = rintf(t);
-                const bool near = fabsf(fabsf(t - qv[i][e]) - 0.5f) <= 1e-4f || tiny;
-                exact |= (uint32_t)near << (4 * i + e);
+                slow = slow || fabsf(t - qv[i][e]) >= 0.4998f;
             }
         }
     }
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(exact != 0) != 0, 0)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(slow) != 0, 0)) {
+        if (slow) {
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            for (int i = 0; i < NF; ++i) {
+                const float xe[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (exact & (1u << (4 * i + e))) qv[i][e] = rintf(xe[e] / scv[i]);
+                for (int e = 0; e < 4; ++e) qv[i][e] = rintf(xe[e] / scv[i]);
+            }
         }
     }
 #pragma unroll
@@ -915,16 +934,7 @@ __device__ __forceinline__ void gemv_stream_body(
     //   A lane (m, g): codes of token m / 3 at k = 16 g .. 16 g + 15 of the
     //   block (rows m >= 3M read a zero block); dword i of A_j is byte i of
     //   code dword j moved to byte m % 3.
-    const int arw = lane & 15;
-    const bool arow = arw < 3 * M;
-    const int8_t *xa = arow ? &xw[wave][(arw / 3) * 64 * kbw + g * 16] : zero16;
-    const int xa_step = arow ? 64 : 0;
-    uint32_t asel[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t dpos = 8u * (uint32_t)(arw % 3);
-        asel[i] = (0x0C0C0C0Cu & ~(0xFFu << dpos)) | ((uint32_t)i << dpos);
-    }
+    // (arw, arow, xa, xa_step and asel are set up before the wait for x)
     const uint32_t lane_off = (uint32_t)lane << 2;
     const char *tb = reinterpret_cast<const char *>(tab);
     const int nsteps = ntw * kbw;  // fragments per wave
