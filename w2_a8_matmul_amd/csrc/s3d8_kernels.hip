@@ -32,6 +32,7 @@
 namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef int32_t v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kTabEntries = 256;
 constexpr int kTabCopies = 64;
@@ -87,6 +88,16 @@ __device__ __forceinline__ void decode16(const uint4 p, const uint32_t lane_off,
         o1[c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x07060302u);
         o2[c] = (int32_t)__builtin_amdgcn_perm(q23, q01, 0x05040100u);
     }
+}
+
+// Position, inside the streaming GEMV's per-wave code slice, of the code of
+// column c (a multiple of 4): blocks of 64 stay in place, and inside a block
+// the 8-byte chunks of columns [0, 8), [16, 24), [32, 40), [48, 56) come
+// first, then those of [8, 16), [24, 32), [40, 48), [56, 64); i.e. column
+// bits 5..3 become bits 4, 3, 5.  The 16 bytes at 16 G of a block are then
+// the codes that A lane group G of the sparse product needs.
+__device__ __forceinline__ int code_pos(int c) {
+    return (c & ~63) | ((c >> 1) & 0x18) | ((c << 2) & 0x20) | (c & 7);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -769,13 +780,14 @@ __device__ __forceinline__ void gemv_stream_body(
     const bool arow = arw < 3 * M;
     const int8_t *xa = arow ? &xw[wave][(arw / 3) * 64 * kbw + g * 16] : zero16;
     const int xa_step = arow ? 64 : 0;
-    uint32_t asel[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t dpos = 8u * (uint32_t)(arw % 3);
-        asel[i] = (0x0C0C0C0Cu & ~(0xFFu << dpos)) | ((uint32_t)i << dpos);
-    }
-    asm volatile("" ::"v"(asel[0]), "v"(asel[1]), "v"(asel[2]), "v"(asel[3]), "v"(xa), "v"(xa_step));
+    // sparsity indices: 2-bit field e of a word is the position, inside its
+    // table dword, that compressed A byte e multiplies; the first product
+    // takes the even bytes to channel d = m % 3 of the row and the odd ones
+    // to position 3 (always zero), the second the other way round
+    const uint32_t dsel = (uint32_t)(arw % 3);
+    const int idx_even = (int)(dsel * 0x11111111u + 0xCCCCCCCCu);
+    const int idx_odd = (int)(0x33333333u + dsel * 0x44444444u);
+    asm volatile("" ::"v"(idx_even), "v"(idx_odd), "v"(xa), "v"(xa_step));
 
     for (int i = tid; i < ntw * kFusedMaxRows * 48; i += kThreads) ybuf[i] = 0;
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
@@ -919,22 +931,32 @@ __device__ __forceinline__ void gemv_stream_body(
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 o |= ((uint32_t)(int32_t)__builtin_amdgcn_fmed3f(qv[i][e], -127.0f, 127.0f) & 0xFFu) << (8 * e);
-            *reinterpret_cast<uint32_t *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]) = scv[i] != 0.0f ? o : 0u;
+            *reinterpret_cast<uint32_t *>(&xw[wave][xm[i] * 64 * kbw + code_pos(4 * xr[i])]) = scv[i] != 0.0f ? o : 0u;
         }
     }
 
     // The products run without the byte transpose of decode16.  A table
-    // lookup gives the dword [w0, w1, w2, 0] of packed byte k; four of them
-    // (bytes 4j .. 4j + 3 of the lane's 16) are used as they are as the B
-    // operand of one v_mfma_i32_16x16x64_i8, whose 64-deep sum then runs
-    // over (byte, channel) pairs.  A row m = 3r + d (token r, channel d)
-    // carries token r's code of each byte in the channel-d position of its
-    // dword and zeros elsewhere, so D[3r + d][n] = sum_k x_rk w_d(k) for
-    // triple n: four MFMAs per 64 x 16 fragment, one accumulator.
-    //   A lane (m, g): codes of token m / 3 at k = 16 g .. 16 g + 15 of the
-    //   block (rows m >= 3M read a zero block); dword i of A_j is byte i of
-    //   code dword j moved to byte m % 3.
-    // (arw, arow, xa, xa_step and asel are set up before the wait for x)
+    // lookup gives the dword [w0, w1, w2, 0] of packed byte k, and eight of
+    // them are used as they are as the B operand of the sparse product
+    // v_smfmac_i32_16x16x128_i8, whose 128-deep sum runs over (byte,
+    // position) pairs.  Row m = 3r + d (token r, channel d) of its A operand
+    // has one non-zero per dword-sized group of K: token r's code of that
+    // byte, at position d.  The instruction takes A compressed (two values
+    // per group of four, each with a 2-bit position in an index register),
+    // so A is just 16 codes per lane; D[3r + d][n] = sum_k x_rk w_d(k) for
+    // triple n: two products per 64 x 16 fragment, one accumulator.
+    //   Operand layout of the instruction (lane l = (row or column l % 16,
+    //   group G = l / 16)): A byte e of lane group G meets B dword
+    //   4 (G / 2) + (e % 8) / 2 of lane group 2 (G % 2) + e / 8.  The first
+    //   product's B dword w is the table dword of lane byte 2w, the second's
+    //   of byte 2w + 1, so A byte e must hold the code of block column
+    //   32 (G % 2) + 16 (e / 8) + 8 (G / 2) + e % 8: the 16 bytes at
+    //   16 G of the block when the codes are stored permuted (code_pos).
+    //   Both products read that one A register; the index word of the first
+    //   sends its even bytes to position d and its odd ones to position 3
+    //   (a zero of every table dword), the second the reverse.
+    // (arw, arow, xa, xa_step and the index words are set up before the
+    // wait for x)
     const uint32_t lane_off = (uint32_t)lane << 2;
     const char *tb = reinterpret_cast<const char *>(tab);
     const int nsteps = ntw * kbw;  // fragments per wave
@@ -948,20 +970,24 @@ __device__ __forceinline__ void gemv_stream_body(
             if (st0 + u >= nsteps) break;  // uniform
             asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pr[u]) : "n"(kStreamSlots - 1) : "memory");
             const u4v p = pr[u];
-            v4i a = {0, 0, 0, 0};
-            if (arow) a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);  // 3M of 16 rows in use
+            // rows m >= 3M read the zero block (xa_step 0)
+            const v4i a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
             const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+            v8i be, bo;  // table dwords of the lane's even / odd bytes
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                v4i bq, aq;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    bq[i] = *reinterpret_cast<const int32_t *>(
+                    const int32_t t = *reinterpret_cast<const int32_t *>(
                         tb + __builtin_amdgcn_perm(pw[jj], lane_off, 0x0C0C0400u + ((uint32_t)i << 8)));
-                    aq[i] = (int32_t)__builtin_amdgcn_perm(0u, (uint32_t)a[jj], asel[i]);
+                    if (i & 1)
+                        bo[2 * jj + (i >> 1)] = t;
+                    else
+                        be[2 * jj + (i >> 1)] = t;
                 }
-                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq, bq, acc, 0, 0, 0);
             }
+            acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, be, acc, idx_even, 0, 0);
+            acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, bo, acc, idx_odd, 0, 0);
             // refill the entry once its bytes are consumed (so the new load
             // writes the same registers and the loop carries no copies)
             ring_load(pr[u], next_off());
@@ -1014,7 +1040,7 @@ __device__ __forceinline__ void gemv_stream_body(
                 const int k = kb0 * 64 + 4 * xr[i];
                 if (i < nf4 && xm[i] < M && k < K)
                     *reinterpret_cast<char4 *>(xq_out + (int64_t)xm[i] * K + k) =
-                        *reinterpret_cast<const char4 *>(&xw[wave][xm[i] * 64 * kbw + 4 * xr[i]]);
+                        *reinterpret_cast<const char4 *>(&xw[wave][xm[i] * 64 * kbw + code_pos(4 * xr[i])]);
             }
         }
     }
