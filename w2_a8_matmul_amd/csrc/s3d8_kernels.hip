@@ -962,7 +962,11 @@ __device__ __forceinline__ void gemv_stream_body(
     const int nsteps = ntw * kbw;  // fragments per wave
 
     v4i acc = {0, 0, 0, 0};
+    v4i a = {0, 0, 0, 0};  // this step's codes (A operand)
     int bl = 0, j = 0;
+    // One loop for every workgroup, without branches around it: a ring
+    // entry that reaches a loop in other registers than it was loaded into
+    // is copied there before its load lands.
 #pragma unroll 1
     for (int st0 = 0; st0 < nsteps; st0 += kStreamSlots) {
 #pragma unroll
@@ -970,8 +974,8 @@ __device__ __forceinline__ void gemv_stream_body(
             if (st0 + u >= nsteps) break;  // uniform
             asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pr[u]) : "n"(kStreamSlots - 1) : "memory");
             const u4v p = pr[u];
-            // rows m >= 3M read the zero block (xa_step 0)
-            const v4i a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
+            // rows m >= 3M keep the zeros set before the loop
+            if (arow) a = *reinterpret_cast<const v4i *>(xa + bl * xa_step);
             const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
             v8i be, bo;  // table dwords of the lane's even / odd bytes
 #pragma unroll
@@ -1008,6 +1012,11 @@ __device__ __forceinline__ void gemv_stream_body(
         }
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The ring registers stay allocated to this point: the compiler takes
+    // an asm load as complete when issued, so without this it could give a
+    // register to another value while a load past the end still writes it.
+#pragma unroll
+    for (int sl = 0; sl < kStreamSlots; ++sl) asm volatile("" ::"v"(pr[sl]));
 
     // epilogue
 #pragma unroll
