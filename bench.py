@@ -66,6 +66,14 @@ def measured_traffic(name, launches_bytes):
     return d.get("hbm_bytes_per_launch")
 
 
+def bootstrap_ci(samples, n_boot=2000, seed=0):
+    """95 % percentile-bootstrap interval of the median of `samples`."""
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, len(samples), size=(n_boot, len(samples)))
+    med = np.median(np.asarray(samples)[idx], axis=1)
+    return float(np.percentile(med, 2.5)), float(np.percentile(med, 97.5))
+
+
 def graph_launch_us(torch, fns, reps, warm_s=0.1):
     """Average duration of one call: the calls fns[0..n-1] are captured back
     to back in one HIP graph, replayed `reps` times between two events on
@@ -174,19 +182,28 @@ def main():
         graph.replay()
     torch.cuda.synchronize()
     log(f"timing {args.steps} steps (graph of {R} steps, R={R} weight copies)")
-    start = torch.cuda.Event(enable_timing=True)
+    # an event after every replay as well: each replay of R launches is one
+    # sample of the per-call time (median and bootstrap interval below);
+    # `value` is the whole timed region
+    nrep = args.steps // R
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps // R):
+    marks[0].record()
+    for i in range(nrep):
         graph.replay()
+        marks[i + 1].record()
     if graph_rem is not None:
         graph_rem.replay()
     end.record()
     torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
+    ms_total = marks[0].elapsed_time(end)
     ms_per_step = ms_total / args.steps
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
+    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) * 1e3 / R for i in range(nrep)])
+    timing = {"samples": int(nrep), "launches_per_sample": R,
+              "per_call_us_median": round(float(np.median(per_call)), 3),
+              "per_call_us_ci95": [round(v, 3) for v in bootstrap_ci(per_call)]}
 
     # dominant kernel: the fused quantise + decode GEMV launched by
     # s3d8_forward.  At M=1 a step is exactly one launch of it, so its
@@ -218,6 +235,31 @@ def main():
         variants["decode"][tag] = {"us": round(v_us, 3), "GBs": round(vbytes / (v_us * 1e-6) / 1e9, 1)}
         log(f"variant {tag}: {v_us:.2f} us -> {variants['decode'][tag]['GBs']} GB/s effective weight bytes")
     del dP, dX
+
+    # ---------------------------------------------------------------- measured ceilings
+    # HBM: a device-to-device copy of 1 GiB (read + write bytes per second),
+    # and a copy of the c1 matrix's size cycling through R buffer pairs (the
+    # same transfer size and cache behaviour as the decode step).  INT8
+    # matrix cores: the rate probe (independent 32x32x32 INT8 MFMA chains on
+    # four waves per SIMD).
+    big = [torch.empty((2 ** 30,), dtype=torch.uint8, device=dev) for _ in range(2)]
+    cp_us = graph_launch_us(torch, [lambda: big[1].copy_(big[0])], 10)
+    del big
+    same = [torch.empty((weight_bytes,), dtype=torch.uint8, device=dev) for _ in range(2 * R)]
+    cs_us = graph_launch_us(torch, [lambda r=r: same[2 * r + 1].copy_(same[2 * r]) for r in range(R)], 10)
+    del same
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    pr_out, pr_ops = s3d8.mfma_rate_probe(2000, 4 * cus, 1, device=dev)
+    pr_us = graph_launch_us(torch, [lambda: s3d8.mfma_rate_probe(2000, 4 * cus, 1, out=pr_out)], 5)
+    ceilings = {"hbm_copy_1GiB_GBs": round(2 * 2 ** 30 / (cp_us * 1e-6) / 1e9, 1),
+                "hbm_copy_c1_size_GBs": round(2 * weight_bytes / (cs_us * 1e-6) / 1e9, 1),
+                "hbm_copy_c1_size_us": round(cs_us, 3),
+                "int8_mfma_probe_TOPS": round(pr_ops / (pr_us * 1e-6) / 1e12, 1),
+                "int8_mfma_probe": f"{4 * cus} workgroups x 4 waves, 2000 rounds of 4 independent "
+                                   f"v_mfma_i32_32x32x32_i8 each"}
+    log(f"ceilings: copy 1 GiB {ceilings['hbm_copy_1GiB_GBs']} GB/s, copy {weight_bytes} B "
+        f"{cs_us:.2f} us ({ceilings['hbm_copy_c1_size_GBs']} GB/s), INT8 MFMA probe "
+        f"{ceilings['int8_mfma_probe_TOPS']} TOPS")
 
     # ---------------------------------------------------------------- one decoder-layer step (c2)
     # the seven linears of a decoder layer at one token, each with its own
@@ -359,6 +401,7 @@ def main():
             "value": round(tops, 2), "unit": "INT8 TOPS", "us_per_launch": round(g_mean_us, 2),
             "roofline": {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS,
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
+                         "frac_of_probe": round(tops / ceilings["int8_mfma_probe_TOPS"], 4),
                          "traffic": measured_traffic("gemm_c3", None),
                          "kernel": "gemm_kernel (fused decode + INT8 MFMA, via s3d8_linear)"},
             "unfused": {"value": round(u_tops, 2), "unit": "INT8 TOPS", "us_per_call": round(u_mean_us, 2),
@@ -414,7 +457,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "gemv_stream_kernel (fused quantise + decode GEMV, via s3d8_forward)", "kernel_us": round(lin_mean_us, 3),
-                     "algorithmic_bytes": kernel_bytes},
+                     "algorithmic_bytes": kernel_bytes,
+                     "frac_of_copy_1GiB": round(achieved / ceilings["hbm_copy_1GiB_GBs"], 4)},
+        "timing": timing,
+        "ceilings": ceilings,
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
         "decoder_layer": layer,

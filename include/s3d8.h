@@ -339,6 +339,19 @@ int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int
 int32_t s3d8_dequant_ex(const uint8_t *packed, const void *table, int32_t format, int64_t N, int64_t K, int8_t *w,
                         void *stream);
 
+/* Matrix-core rate probe: a measurement utility for reading the GEMM's
+ * INT8 rate against what the matrix cores sustain, not part of the method.
+ * `workgroups` workgroups of 256 threads (4 waves) each run `iters` rounds
+ * of four independent v_mfma_i32_32x32x32_i8 (a 32 x 32 x 32 INT8 product
+ * into INT32, 65536 integer operations) on register operands whose bytes
+ * all equal v; thread t of workgroup w then stores 2048 * v^2 * iters
+ * (mod 2^32) to out[256 w + t].  A call performs
+ * workgroups * 4 * 4 * iters * 65536 operations.
+ *   out   out, device int32 [256 * workgroups], 4-B aligned.
+ * Errors: INVALID_ARG (out NULL, iters < 1, workgroups outside
+ * [1, 65536], v outside [-128, 127]), ALIGN, DEVICE, HIP. */
+int32_t s3d8_mfma_rate_probe(int32_t iters, int32_t workgroups, int32_t v, int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

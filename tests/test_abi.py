@@ -129,6 +129,17 @@ def test_dequant_validation():
     assert L.s3d8_dequant(A16, A16, 0, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
 
 
+def test_mfma_rate_probe_validation():
+    L = _lib.lib()
+    assert L.s3d8_mfma_rate_probe(1, 1, 1, None, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(0, 1, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(1, 0, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(1, 65537, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(1, 1, 128, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(1, 1, -129, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_mfma_rate_probe(1, 1, 1, A16 + 2, None) == _lib.S3D8_ERR_ALIGN
+
+
 def test_linear_unfused_validation():
     L = _lib.lib()
     assert L.s3d8_unfused_workspace_bytes(10, 64) == 2048  # 12 channels: one 32-channel fragment

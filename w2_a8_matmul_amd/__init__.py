@@ -349,6 +349,22 @@ def dequant(packed, centroids, N: int, w=None, fmt: str = "s3d8"):
     return w
 
 
+def mfma_rate_probe(iters: int, workgroups: int, v: int = 1, out=None, device="cuda"):
+    """Matrix-core rate probe (a measurement utility): `workgroups` x 4
+    waves each run `iters` rounds of four independent 32x32x32 INT8 MFMAs;
+    every word of out (int32 [256 * workgroups]) becomes 2048 v^2 iters
+    (mod 2^32).  Returns (out, integer operations performed)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((256 * workgroups,), dtype=torch.int32, device=device)
+    _dev_check(out, torch.int32, "out")
+    if out.numel() < 256 * workgroups:
+        raise ValueError("out must hold 256 * workgroups int32")
+    with torch.cuda.device(out.device):
+        call("s3d8_mfma_rate_probe", iters, workgroups, v, out.data_ptr(), _stream(out))
+    return out, workgroups * 4 * 4 * iters * 65536
+
+
 class PackedLinear:
     """An S3D8 weight matrix resident in device memory, in the tiled layout."""
 

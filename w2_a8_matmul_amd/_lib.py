@@ -46,6 +46,7 @@ SIGNATURES = {
     "s3d8_forward_ex": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P, _P, _P]),
     "s3d8_linear_unfused_ex": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P]),
     "s3d8_dequant_ex": (_I32, [_P, _P, _I32, _I64, _I64, _P, _P]),
+    "s3d8_mfma_rate_probe": (_I32, [_I32, _I32, _I32, _P, _P]),
 }
 
 

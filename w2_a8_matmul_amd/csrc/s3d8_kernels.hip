@@ -1508,6 +1508,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     store_tile_rows<true, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
+// --------------------------------------------------------------- matrix-core rate probe
+
+// A measurement utility, not part of the method: the INT8 matrix-core rate
+// this part sustains, against which the fused GEMM is read.  Each wave runs
+// `iters` rounds of four independent v_mfma_i32_32x32x32_i8 (one chain per
+// accumulator, so an instruction never waits for the previous one's result)
+// on register operands whose bytes all equal v; nothing else is in the loop.
+// Every accumulator element gains 32 v^2 per round, so lane t of workgroup w
+// stores 4 x 16 x 32 v^2 iters = 2048 v^2 iters (mod 2^32).
+constexpr int kRateThreads = 256;
+__global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(int iters, int v, int32_t *__restrict__ out) {
+    const int32_t w = (int32_t)(((uint32_t)v & 0xFFu) * 0x01010101u);
+    const v4i a = {w, w, w, w};
+    v16i acc[4] = {};
+#pragma unroll 1
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, a, acc[c], 0, 0, 0);
+    }
+    uint32_t sum = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum += (uint32_t)acc[c][r];
+    out[(int64_t)blockIdx.x * kRateThreads + threadIdx.x] = (int32_t)sum;
+}
+
 // --------------------------------------------------------------- dequant
 
 // Standalone S3D8 -> channel-INT8 decode (the blog's dequantisation kernel).
@@ -2311,6 +2338,18 @@ int32_t s3d8_dequant_ex(const uint8_t *packed, const void *table, int32_t format
     int rc = check_variant(format, S3D8_OUT_F32);
     if (rc) return rc;
     return dequant_impl(packed, table, format == S3D8_FORMAT_3D8, N, K, w, stream);
+}
+
+int32_t s3d8_mfma_rate_probe(int32_t iters, int32_t workgroups, int32_t v, int32_t *out, void *stream) {
+    if (!out) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    if (iters < 1 || workgroups < 1 || workgroups > 65536 || v < -128 || v > 127)
+        return s3d8::fail(S3D8_ERR_INVALID_ARG, "iters >= 1, 1 <= workgroups <= 65536, -128 <= v <= 127");
+    if (reinterpret_cast<uintptr_t>(out) & 3u) return s3d8::fail(S3D8_ERR_ALIGN, "out must be 4-byte aligned");
+    int rc = check_device(nullptr);
+    if (rc) return rc;
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)workgroups), dim3(kRateThreads), 0, (hipStream_t)stream,
+                       (int)iters, (int)v, out);
+    return launch_status();
 }
 
 }  // extern "C"
