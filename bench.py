@@ -47,10 +47,15 @@ def log(msg):
 
 
 def kernel_source_sha():
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "w2_a8_matmul_amd", "csrc", "s3d8_kernels.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the kernel source with comments and whitespace removed, so
+    that counters taken on it stay valid across comment-only edits."""
+    import re
+    with open(os.path.join(ROOT, "w2_a8_matmul_amd", "csrc", "s3d8_kernels.hip")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic(name, launches_bytes):

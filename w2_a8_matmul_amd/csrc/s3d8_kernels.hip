@@ -568,16 +568,18 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(
 //
 // At one token the layer is a single read of the packed matrix; what limits
 // it is how early that read starts, how long the chain in front of the first
-// decode is, and how evenly the bytes are spread.  Every wave issues, before
-// anything else, one load of the centroid row its lanes need for the table,
-// its share of the fp32 activations, and its first kStreamSlots weight
-// fragments (16 bytes per lane each, a ring of registers: a lane's bytes are
-// its own, so they need not pass through LDS).  The table is then built from
-// registers, the row absmax is reduced with DPP, and one barrier later the
-// activations are quantised and the decode starts.  The main loop has no
-// barriers: each step takes the oldest fragment, refills its ring entry
-// kStreamSlots steps ahead, looks up the 16 packed bytes and runs four
-// v_mfma_i32_16x16x64_i8 on the raw lookup dwords (see the loop).
+// decode is, and how evenly the bytes are spread.  Every wave issues first
+// one load of the centroid row its lanes need for the table and its share of
+// the fp32 activations, then (after a barrier that lets every wave's small
+// loads go ahead) its first two weight fragments (16 bytes per lane each,
+// into a ring of registers: a lane's bytes are its own, so they need not
+// pass through LDS).  The table is then built from registers, the row
+// absmax is reduced with DPP, and after one workgroup barrier the last two
+// fragments of the ring are issued, the activations are quantised and the
+// decode starts.  The main loop has no barriers: each step takes the oldest
+// fragment, looks up its 16 packed bytes, runs two sparse products
+// v_smfmac_i32_16x16x128_i8 on the raw lookup dwords (see the loop) and
+// refills the ring entry kStreamSlots steps ahead.
 //
 // Work split: a workgroup takes tiles of 16 triples (its index, + grid,
 // ...), its 16 waves split K into ranges of kbw 64-column blocks.  Partial
