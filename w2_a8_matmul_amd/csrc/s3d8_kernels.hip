@@ -1971,8 +1971,10 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     if (count > 1 && (f3d8 || obf)) return false;
     const int64_t M = items[0].M;
     if (M < 1 || M > kFusedMaxRows) return false;
-    // 16 waves (8 were measured slower at K = 4096: the shorter prologue is
-    // outweighed by half as many waves hiding the decode's LDS latency)
+    // 16 waves (8 were measured slower at K = 4096, with the dense product
+    // and again with the sparse one, 8.3 against 7.3 us: the shorter
+    // prologue is outweighed by half as many waves hiding the lookups' LDS
+    // latency; 8 waves also take K = 14336 out of the M * kbw <= 16 range)
     constexpr int W = 16;
     int64_t tiles[kStreamBatch], Ks[kStreamBatch];
     for (int p = 0; p < count; ++p) {
