@@ -529,6 +529,30 @@ def test_linear_unfused_matches_fused_full(gpu):
     np.testing.assert_array_equal(y_u, y_f)
 
 
+def test_prefill_paths_160_row_tiles_ragged(gpu):
+    """M = 2000 (12.5 tiles of 160 rows) and N = 14335 (ragged triples), the
+    size at which both prefill GEMMs take 5 row tiles per wave: sampled
+    entries against the oracle, and the two paths against each other in
+    full."""
+    M, K, N = 2000, 1024, 14335
+    C, alpha, packed = random_format([2080, M, K, N], N, K)
+    x = workloads.gaussian_matrix([2081, M, K], M, K)
+    xq_f, xs_f, acc_f, y_f = run_linear(x, C, alpha, packed, N, gpu)
+    _, _, acc_u, y_u = run_linear(x, C, alpha, packed, N, gpu, unfused=True)
+    np.testing.assert_array_equal(acc_u, acc_f)
+    np.testing.assert_array_equal(y_u, y_f)
+    xq_r, xs_r = oracle.quant_act(x)
+    np.testing.assert_array_equal(xq_f, xq_r)
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2082])))
+    ms = list(g.integers(0, M, 256)) + [0, M - 1, 1919, 1920, 1999]
+    ns = list(g.integers(0, N, 256)) + [N - 1, 0, 14333, N - 1, 14334]
+    ref = np.array([oracle.acc_one(xq_r[m], packed, C, K, n) for m, n in zip(ms, ns)], np.int64)
+    np.testing.assert_array_equal(acc_u[np.array(ms), np.array(ns)].astype(np.int64), ref)
+    for i, (m, n) in enumerate(zip(ms, ns)):
+        y_r = oracle.epilogue(ref[i:i + 1].astype(np.int32).reshape(1, 1), xs_r[m:m + 1], alpha[n:n + 1], 1)
+        check_y(y_u[m, n:n + 1].reshape(1, 1), y_r)
+
+
 def test_linear_unfused_workspace_reuse(gpu):
     """A workspace larger than needed, reused by a second, smaller call."""
     K1, N1, K2, N2 = 1040, 97, 256, 48

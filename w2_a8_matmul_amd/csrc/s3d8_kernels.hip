@@ -1612,22 +1612,39 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
 }
 
 // INT8 x INT8 GEMM on v_mfma_i32_32x32x32_i8: y = (xs * acc) * alpha.
-// Workgroup tile 128 token rows x 384 channels, 4 waves side by side along
-// N, wave tile 128 x 96 (4 x 3 accumulators of 32 x 32).  Per 64-column
-// block the activation tile (XOR-swizzled as in the fused GEMM) and the
-// weight fragments (already in B-operand lane order, 1 KiB contiguous per
-// load) are copied into a five-slot LDS ring four blocks ahead; the MFMAs
-// read both operands from LDS.
-constexpr int kI8Slots = 5;
-constexpr int kI8Ahead = kI8Slots - 1;
+// Workgroup tile 32 RT token rows x 384 channels, 4 waves side by side
+// along N, wave tile 32 RT x 96 (RT x 3 accumulators of 32 x 32).  Per
+// 64-column block the activation tile (XOR-swizzled as in the fused GEMM)
+// and the weight fragments (already in B-operand lane order, 1 KiB
+// contiguous per load) are copied into an LDS ring of kSlots slots,
+// kSlots - 1 blocks ahead (five slots at RT = 4, four at RT = 5, whose
+// larger activation tile leaves room for no more); the MFMAs read both
+// operands from LDS.
+template <int N>
+__device__ __forceinline__ void vm_wait_imm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void vm_wait_imm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
-template <bool kAcc, bool kBF>
+template <int RT, bool kAcc, bool kBF>
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                       int M, int K, int N, int NP, const int8_t *__restrict__ w8,
                                                       const uint16_t *__restrict__ scales, void *__restrict__ y,
                                                       int32_t *__restrict__ acc_out, int nbm, int nbn) {
-    __shared__ __attribute__((aligned(16))) int8_t abuf[kI8Slots][kGemmBM * 64];
-    __shared__ __attribute__((aligned(16))) int8_t bbuf[kI8Slots][4 * 6 * 1024];
+    static_assert(RT == 4 || RT == 5, "4 or 5 row tiles per wave");
+    constexpr int BM = 32 * RT;
+    constexpr int kSlots = RT == 4 ? 5 : 4;
+    constexpr int kAhead = kSlots - 1;
+    constexpr int NA = (2 * RT + 3) / 4;  // activation loads per wave and block
+    constexpr int ND = NA + 6;            // all loads per wave and block
+    // activation slots, then (only when 4 NA > 2 RT) 1 KiB that loads past
+    // the tile fill
+    constexpr int kSpill = (4 * NA > 2 * RT) ? 1024 : 0;
+    __shared__ __attribute__((aligned(16))) int8_t abuf[kSlots * BM * 64 + kSpill];
+    __shared__ __attribute__((aligned(16))) int8_t bbuf[kSlots][4 * 6 * 1024];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1636,20 +1653,23 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 
     int bm, bn;
     if (!gemm_tile(nbm, nbn, bm, bn)) return;
-    const int row0 = bm * kGemmBM;
+    const int row0 = bm * BM;
     const int ch0 = bn * 384 + wave * 96;  // first channel of this wave
 
     const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
     const v4i rw = rsrc_words(w8, (uint32_t)((NP + 31) / 32) * (uint32_t)KB * 2048u);
 
-    uint32_t aoff[2];
-    int acol[2];
+    // activation copy: wave w moves 16-byte units u = 64 (NA w + j) + lane
+    // of the BM x 64 tile (row u / 4, chunk (u % 4) ^ ((row / 4) % 4));
+    // units past the tile (4 NA > 2 RT) read nothing into `spill`
+    uint32_t aoff[NA];
+    int acol[NA];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int u = 64 * (2 * wave + j) + lane;
+    for (int j = 0; j < NA; ++j) {
+        const int u = 64 * (NA * wave + j) + lane;
         const int row = u >> 2;
         const int chunk = (u & 3) ^ ((row >> 2) & 3);
-        aoff[j] = row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        aoff[j] = row < BM && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
         acol[j] = 16 * chunk;
     }
     // B operand (column tile ct, k-half kh) of lane L: 16 bytes at unit
@@ -1660,13 +1680,15 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         const int ctile = ch0 / 32 + ct;
         boff[ct] = 32 * ctile < NP ? (uint32_t)ctile * (uint32_t)KB * 2048u + 16u * lane : kOOB;
     }
-    const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), bbase = S3D8_LDS_OFFSET(&bbuf[0][0]);
-    // eight loads per wave and block, also past the end (they read nothing)
+    const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0]), bbase = S3D8_LDS_OFFSET(&bbuf[0][0]);
+    const uint32_t sbase = abase + (uint32_t)(kSlots * BM * 64);
+    // ND loads per wave and block, also past the end (they read nothing), so
+    // that every wait below counts the same
     auto issue = [&](int kb, int slot) {
         const bool live = kb < KB;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            load_to_lds16(abase + (uint32_t)(kGemmBM * 64) * slot + 1024u * (2 * wave + j),
+        for (int j = 0; j < NA; ++j)
+            load_to_lds16(NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j) : sbase,
                           (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
 #pragma unroll
         for (int ct = 0; ct < 3; ++ct)
@@ -1682,24 +1704,24 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     const int ard0 = c32 * 64 + 16 * (h ^ swz), ard1 = c32 * 64 + 16 * ((h ^ swz) ^ 2);
 
 #pragma unroll
-    for (int sl = 0; sl < kI8Ahead; ++sl) issue(sl, sl);
+    for (int sl = 0; sl < kAhead; ++sl) issue(sl, sl);
 
-    v16i acc[kGemmRT][3];
+    v16i acc[RT][3];
 #pragma unroll
-    for (int i = 0; i < kGemmRT; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
         for (int d = 0; d < 3; ++d) acc[i][d] = v16i{};
 
-    // operands of one block: A for 4 row tiles x 2 k-halves, B for 3 column
-    // tiles x 2 k-halves (14 x 16 bytes per lane)
+    // operands of one block: A for RT row tiles x 2 k-halves, B for 3
+    // column tiles x 2 k-halves (2 RT + 6 times 16 bytes per lane)
     struct Ops {
-        v4i a[kGemmRT][2], b[3][2];
+        v4i a[RT][2], b[3][2];
     };
     auto read_ops = [&](Ops &o, int slot) {
-        const int8_t *ab = abuf[slot];
+        const int8_t *ab = abuf + slot * (BM * 64);
         const int8_t *bb = bbuf[slot] + 6144 * wave + 16 * lane;
 #pragma unroll
-        for (int i = 0; i < kGemmRT; ++i) {
+        for (int i = 0; i < RT; ++i) {
             o.a[i][0] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard0);
             o.a[i][1] = *reinterpret_cast<const v4i *>(ab + 2048 * i + ard1);
         }
@@ -1712,42 +1734,42 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int i = 0; i < kGemmRT; ++i)
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
                 for (int ct = 0; ct < 3; ++ct)
                     acc[i][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(o.a[i][kh], o.b[ct][kh], acc[i][ct], 0, 0, 0);
     };
 
     // block kb (operands already in registers `cur`): wait until blocks <=
-    // kb + 1 are in LDS for every wave (16 loads = blocks kb + 2, kb + 3 may
-    // still fly), refill the slot of block kb - 1 with block kb + 4, read
-    // block kb + 1's operands into `nxt` while the MFMAs of block kb run
-    static_assert(kI8Ahead == 4, "the vmcnt immediates below assume four blocks in flight");
+    // kb + 1 are in LDS for every wave (the loads of blocks kb + 2 ..
+    // kb + kAhead - 1 may still fly), refill the slot of block kb - 1 with
+    // block kb + kAhead, read block kb + 1's operands into `nxt` while the
+    // MFMAs of block kb run
     auto block = [&](const Ops &cur, Ops &nxt, int kb, int slot) {
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(kb + kI8Ahead, slot == 0 ? kI8Slots - 1 : slot - 1);
-        read_ops(nxt, slot == kI8Slots - 1 ? 0 : slot + 1);
+        vm_wait_imm_barrier<(kAhead - 2) * ND>();
+        issue(kb + kAhead, slot == 0 ? kSlots - 1 : slot - 1);
+        read_ops(nxt, slot == kSlots - 1 ? 0 : slot + 1);
         mfmas(cur);
-        // interleave the 14 operand reads of the next block with the first
-        // MFMAs of this one, so that their LDS latency hides behind them
+        // interleave the 2 RT + 6 operand reads of the next block with the
+        // first MFMAs of this one, so that their LDS latency hides behind them
 #pragma unroll
-        for (int q = 0; q < 14; ++q) {
+        for (int q = 0; q < 2 * RT + 6; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6 * RT - (2 * RT + 6), 0);
     };
 
     Ops o0, o1;
-    asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");  // block 0 in LDS for every wave
+    vm_wait_imm_barrier<(kAhead - 1) * ND>();  // block 0 in LDS for every wave
     read_ops(o0, 0);
     int kb = 0, slot = 0;
 #pragma unroll 1
     for (; kb + 1 < KB; kb += 2) {
         block(o0, o1, kb, slot);
-        slot = slot == kI8Slots - 1 ? 0 : slot + 1;
+        slot = slot == kSlots - 1 ? 0 : slot + 1;
         block(o1, o0, kb + 1, slot);
-        slot = slot == kI8Slots - 1 ? 0 : slot + 1;
+        slot = slot == kSlots - 1 ? 0 : slot + 1;
     }
     if (kb < KB) block(o0, o1, kb, slot);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1763,7 +1785,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         coff[ct] = ch < N ? 4u * (uint32_t)ch : kOOB;
         sc[ct] = bf16_to_f32(bload2(rsc, ch < N ? 2u * (uint32_t)ch : kOOB));
     }
-    store_tile_rows<false, kAcc, kGemmRT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+    store_tile_rows<false, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- encode on the device
@@ -2279,16 +2301,26 @@ int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_
     hipLaunchKernelGGL(dequant_tiled_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0, (hipStream_t)stream,
                        tiled, reinterpret_cast<const uint32_t *>(table), (int)K, (int)T, KB, nchunks, workspace,
                        (int)f3d8);
-    const int nbm = (int)((M + kGemmBM - 1) / kGemmBM);
     const int nbn = (int)((3 * T + 383) / 384);
+    // 4 or 5 row tiles per wave, as for the fused GEMM: the one that needs
+    // fewer workgroup rounds, counted in units of row-tile work
+    auto cost = [&](int rt) {
+        const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
+        return (tiles + cus - 1) / cus * rt;
+    };
+    const int rt = cost(5) < cost(4) ? 5 : 4;
+    const int nbm = (int)((M + 32 * rt - 1) / (32 * rt));
     const int64_t nwg = (int64_t)nbm * nbn;
     const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
     if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
     typedef void (*I8Fn)(const int8_t *, const float *, int, int, int, int, const int8_t *, const uint16_t *, void *,
                          int32_t *, int, int);
-    static const I8Fn fns[2][2] = {{gemm_i8_kernel<false, false>, gemm_i8_kernel<false, true>},
-                                   {gemm_i8_kernel<true, false>, gemm_i8_kernel<true, true>}};
-    hipLaunchKernelGGL(fns[acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs,
+    static const I8Fn fns[2][2][2] = {
+        {{gemm_i8_kernel<4, false, false>, gemm_i8_kernel<4, false, true>},
+         {gemm_i8_kernel<4, true, false>, gemm_i8_kernel<4, true, true>}},
+        {{gemm_i8_kernel<5, false, false>, gemm_i8_kernel<5, false, true>},
+         {gemm_i8_kernel<5, true, false>, gemm_i8_kernel<5, true, true>}}};
+    hipLaunchKernelGGL(fns[rt == 5][acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs,
                        (int)M, (int)K, (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
     return launch_status();
 }
