@@ -310,6 +310,39 @@ def main():
             f"-> {gbs:.1f} GB/s effective weight bytes")
         del lay
 
+    # ---------------------------------------------------------------- lm_head decode step (c4, M=1)
+    # the same streaming GEMV over the 175 MB lm_head matrix (K=4096,
+    # N=128256), where the fixed costs of a launch (start-up, prologue, the
+    # last tiles) weigh far less than on the 19.6 MB c1 matrix.  Uniform
+    # random bytes, table and bf16 scales: a kernel's time does not depend
+    # on the byte values, and packing 525 M weights would take the bench
+    # minutes.  Four weight copies (700 MB) cycle as above.
+    lm_head = None
+    if not args.no_layer:
+        lh = workloads.C4[0]
+        Tl = s3d8.num_triples(lh.N)
+        lbytes = s3d8.format_bytes(lh.N, lh.K)
+        Pl = torch.from_numpy(workloads.random_packed(lh.config_id, Tl, lh.K, lh.matrix_id)).to(dev)
+        dPl = [s3d8.tile(Pl, lh.N) for _ in range(4)]
+        del Pl
+        dCl = torch.from_numpy(workloads.random_centroids(lh.config_id, lh.matrix_id)).to(dev)
+        dSl = torch.from_numpy(workloads.random_scales_bf16(lh.config_id, 3 * Tl, lh.matrix_id).view(np.int16)).to(dev)
+        xl = torch.from_numpy(workloads.activations(lh)).to(dev)
+        yl = torch.empty((1, lh.N), dtype=torch.float32, device=dev)
+        xql = torch.empty((1, lh.K), dtype=torch.int8, device=dev)
+        xsl = torch.empty((1,), dtype=torch.float32, device=dev)
+        fns = [lambda r=r: s3d8.forward(xl, dPl[r], dCl, dSl, lh.N, y=yl, xq=xql, xs=xsl) for r in range(4)]
+        fns[0]()
+        l_us = graph_launch_us(torch, fns, 10)
+        l_gbs = lbytes / (l_us * 1e-6) / 1e9
+        lm_head = {"workload": f"{lh.name}: M=1 K={lh.K} N={lh.N}, uniform random S3D8 bytes",
+                   "effective_weight_bytes": lbytes, "us": round(l_us, 2), "GBs": round(l_gbs, 1),
+                   "frac_hbm": round(l_gbs / HBM_PEAK_GBS, 4),
+                   "frac_of_copy_1GiB": round(l_gbs / ceilings["hbm_copy_1GiB_GBs"], 4)}
+        log(f"lm_head decode: {l_us:.2f} us -> {l_gbs:.1f} GB/s effective weight bytes "
+            f"({lm_head['frac_hbm'] * 100:.1f}% of HBM peak)")
+        del dPl
+
     # ---------------------------------------------------------------- standalone dequant + copy baselines
     # the pages' own kernel measurement: S3D8 -> channel-INT8 dequantisation
     # against a plain copy of the same matrix in INT8, on the c1 gate/up
@@ -469,6 +502,7 @@ def main():
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
         "decoder_layer": layer,
+        "lm_head": lm_head,
         "encode": encode,
         "dequant": dequant,
         "variants": variants,
