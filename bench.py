@@ -239,6 +239,27 @@ def main():
         vbytes = weight_bytes + (768 - 96 if fmt == "3d8" else 0)
         variants["decode"][tag] = {"us": round(v_us, 3), "GBs": round(vbytes / (v_us * 1e-6) / 1e9, 1)}
         log(f"variant {tag}: {v_us:.2f} us -> {variants['decode'][tag]['GBs']} GB/s effective weight bytes")
+    # ---------------------------------------------------------------- c1 at M = 4 and 8
+    # the other token counts of the c1 decode step: M = 4 through the same
+    # one-launch streaming kernel, M = 8 as quantisation plus the GEMV with
+    # the token rows as the MFMA's A operand (s3d8_forward picks both)
+    decode_m = {}
+    for mm in (4, 8):
+        lm_ = workloads.C1[mm]
+        xm_ = [torch.from_numpy(workloads.activations(lm_)).to(dev) for _ in range(R)]
+        ym_ = torch.empty((mm, N), dtype=torch.float32, device=dev)
+        xqm = torch.empty((mm, K), dtype=torch.int8, device=dev)
+        xsm = torch.empty((mm,), dtype=torch.float32, device=dev)
+        fns = [lambda r=r, xm_=xm_, ym_=ym_, xqm=xqm, xsm=xsm: s3d8.forward(xm_[r], dP[r], dC, dS, N, y=ym_, xq=xqm,
+                                                                            xs=xsm) for r in range(R)]
+        fns[0]()
+        m_us = graph_launch_us(torch, fns, 10)
+        decode_m[str(mm)] = {"us": round(m_us, 3), "GBs": round(weight_bytes / (m_us * 1e-6) / 1e9, 1),
+                             "path": "one streaming launch" if mm <= 4 else "quant_act + token-row GEMV"}
+        log(f"c1 decode M={mm}: {m_us:.2f} us -> {decode_m[str(mm)]['GBs']} GB/s effective weight bytes "
+            f"({decode_m[str(mm)]['path']})")
+        del xm_
+    variants["decode_m"] = decode_m
     del dP, dX
 
     # ---------------------------------------------------------------- measured ceilings
