@@ -277,7 +277,7 @@ def test_linear_repeated_calls_are_identical(gpu):
 
 
 # ------------------------------------------------------------------ forward (quantise + linear)
-FWD = [(m, k, n) for m in (1, 2, 3, 4, 5, 16) for (k, n) in [(16, 3), (80, 50), (1040, 97), (4096, 300),
+FWD = [(m, k, n) for m in (1, 2, 3, 4, 5, 6, 7, 8, 16) for (k, n) in [(16, 3), (80, 50), (1040, 97), (4096, 300),
                                                             (14336, 64), (16384, 48)]]
 
 
