@@ -1441,8 +1441,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // of A(kb) x B(kb) in 2 RT groups of three, with the operands of block
     // kb + 1 prepared between them.  Group g carries: the raw weights (g = 0),
     // A row tile i (g = i % 4), the lookups of dwords 2 (g - 1) and 2 (g - 1)
-    // + 1, and the transposes of dwords 2 (g - 3) and 2 (g - 3) + 1, so that
-    // every LDS read has two groups of MFMAs to land behind.  Inside a group
+    // + 1, and the transposes of dwords 2 (g - TR0) and 2 (g - TR0) + 1, so
+    // that every lookup has TR0 - 1 groups of MFMAs to land behind (TR0 = 6
+    // of the ten groups at RT = 5: five groups, about 1.5 % faster at c3 than
+    // two, which is all that the eight groups at RT = 4 leave room for).
+    // Inside a group
     // each MFMA is followed by a share of the VALU and LDS work, since one
     // wave per SIMD only overlaps what lies between its MFMAs; sched_barrier
     // keeps the compiler from regrouping across groups.
@@ -1469,9 +1472,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
                 lookups(wn, 2 * (g - 1), q[2 * (g - 1)]);
                 lookups(wn, 2 * (g - 1) + 1, q[2 * (g - 1) + 1]);
             }
-            if (g >= 3 && g <= 6) {
-                transpose(q[2 * (g - 3)], bnx, 2 * (g - 3));
-                transpose(q[2 * (g - 3) + 1], bnx, 2 * (g - 3) + 1);
+            constexpr int TR0 = RT == 5 ? 6 : 3;
+            if (g >= TR0 && g <= TR0 + 3) {
+                transpose(q[2 * (g - TR0)], bnx, 2 * (g - TR0));
+                transpose(q[2 * (g - TR0) + 1], bnx, 2 * (g - TR0) + 1);
             }
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
