@@ -1440,11 +1440,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // refill the slot of block kb - 1 with block kb + 4, then the 6 RT MFMAs
     // of A(kb) x B(kb) in 2 RT groups of three, with the operands of block
     // kb + 1 prepared between them.  Group g carries: the raw weights (g = 0),
-    // A row tile i (g = i % 4), the lookups of dwords 2 (g - 1) and 2 (g - 1)
-    // + 1, and the transposes of dwords 2 (g - TR0) and 2 (g - TR0) + 1, so
-    // that every lookup has TR0 - 1 groups of MFMAs to land behind (TR0 = 6
-    // of the ten groups at RT = 5: five groups, about 1.5 % faster at c3 than
-    // two, which is all that the eight groups at RT = 4 leave room for).
+    // A row tile i (g = i % 4), the lookups of dwords 2 (g - LK0) and
+    // 2 (g - LK0) + 1, and the transposes of dwords 2 (g - TR0) and
+    // 2 (g - TR0) + 1.  At RT = 5 (ten groups) LK0 = 2 and TR0 = 6: the raw
+    // weights have two groups of MFMAs to land behind and every lookup four
+    // (measured at c3 about 2.5 % faster than LK0 = 1, TR0 = 3, which is all
+    // that the eight groups at RT = 4 leave room for).
     // Inside a group
     // each MFMA is followed by a share of the VALU and LDS work, since one
     // wave per SIMD only overlaps what lies between its MFMAs; sched_barrier
@@ -1468,9 +1469,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 #pragma unroll
             for (int r = 0; r < RT; ++r)
                 if (g == r % 4) read_a(an, next, r);
-            if (g >= 1 && g <= 4) {
-                lookups(wn, 2 * (g - 1), q[2 * (g - 1)]);
-                lookups(wn, 2 * (g - 1) + 1, q[2 * (g - 1) + 1]);
+            constexpr int LK0 = RT == 5 ? 2 : 1;
+            if (g >= LK0 && g <= LK0 + 3) {
+                lookups(wn, 2 * (g - LK0), q[2 * (g - LK0)]);
+                lookups(wn, 2 * (g - LK0) + 1, q[2 * (g - LK0) + 1]);
             }
             constexpr int TR0 = RT == 5 ? 6 : 3;
             if (g >= TR0 && g <= TR0 + 3) {
