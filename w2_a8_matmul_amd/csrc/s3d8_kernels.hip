@@ -1179,13 +1179,16 @@ __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
 //
 // kBF: y is bfloat16 (round to nearest even of the fp32 value, as the
 // blog's fused kernel writes its results); every channel goes out as its
-// own 2-byte store.
-template <bool kTriple, bool kAcc, int RT, bool kBF = false>
+// own 2-byte store.  kNT: the stores of y are non-temporal (they stream past
+// the caches; measured faster for the plain INT8 GEMM, slower for the fused
+// one).
+template <bool kTriple, bool kAcc, int RT, bool kBF = false, bool kNT = false>
 __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const float *__restrict__ xs, int M,
                                                 int N, int row0, int h, const float (&sc)[3], const uint32_t (&coff)[3],
                                                 void *__restrict__ y, int32_t *__restrict__ acc_out) {
     const int nrows = min(M - row0, 32 * RT);
     const uint32_t rowb = 4u * (uint32_t)N;
+    constexpr int kYAux = kNT ? 2 : 0;  // cache policy bits of the y stores (2: non-temporal)
     const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
     float4 sx[RT][4];
 #pragma unroll
@@ -1215,7 +1218,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(outf(i, v, j)), ry,
-                                                          (ybase[j] + (uint32_t)r * yrowb) | dead(r), 0, 0);
+                                                          (ybase[j] + (uint32_t)r * yrowb) | dead(r), 0, kYAux);
                     if constexpr (kAcc)
                         __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra,
                                                               (base[j] + (uint32_t)r * rowb) | dead(r), 0, 0);
@@ -1234,7 +1237,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
             for (int v = 0; v < 16; ++v) {
                 const int r = 32 * i + 8 * (v >> 2) + (v & 3);
                 const uint32_t off = (base3 + (uint32_t)r * rowb) | dead(r);
-                __builtin_amdgcn_raw_buffer_store_b96(u3{out(i, v, 0), out(i, v, 1), out(i, v, 2)}, ry, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b96(u3{out(i, v, 0), out(i, v, 1), out(i, v, 2)}, ry, off, 0, kYAux);
                 if constexpr (kAcc)
                     __builtin_amdgcn_raw_buffer_store_b96(
                         u3{(uint32_t)acc[i][0][v], (uint32_t)acc[i][1][v], (uint32_t)acc[i][2][v]}, ra, off, 0, 0);
@@ -1249,7 +1252,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const uint32_t off = (base[j] + (uint32_t)r * rowb) | d;
-                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, kYAux);
                     if constexpr (kAcc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra, off, 0, 0);
                 }
             }
@@ -1262,7 +1265,7 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
 #pragma unroll
                 for (int j = 0; j < 3; ++j) {
                     const uint32_t off = (base[j] + (uint32_t)r * rowb) | dead(r);
-                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(out(i, v, j), ry, off, 0, kYAux);
                     if constexpr (kAcc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][j][v], ra, off, 0, 0);
                 }
             }
@@ -1791,7 +1794,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
         coff[ct] = ch < N ? 4u * (uint32_t)ch : kOOB;
         sc[ct] = bf16_to_f32(bload2(rsc, ch < N ? 2u * (uint32_t)ch : kOOB));
     }
-    store_tile_rows<false, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+    store_tile_rows<false, kAcc, RT, kBF, true>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- encode on the device
