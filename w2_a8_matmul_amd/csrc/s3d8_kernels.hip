@@ -1086,11 +1086,11 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamB
 // Prefill GEMM for many token rows: INT8 activations x decoded S3D8 weights
 // on v_mfma_i32_32x32x32_i8 (INT32 accumulation).
 //
-// Workgroup tile = 128 token rows x 128 channel triples (384 output
-// channels); 4 waves side by side along N, each 128 rows x 32 triples =
-// 4 row tiles x 3 channels of the triple = 12 accumulators of 32 x 32
-// (192 AGPRs, one wave per SIMD).  Per 64-column block of K:
-//  - activations (128 x 64 INT8) and the packed weights (128 triples x 64)
+// Workgroup tile = 32 RT token rows x 128 channel triples (384 output
+// channels), RT = 4 or 5; 4 waves side by side along N, each 32 RT rows x
+// 32 triples = RT row tiles x 3 channels of the triple = 3 RT accumulators
+// of 32 x 32 (192 or 240 AGPRs, one wave per SIMD).  Per 64-column block of K:
+//  - activations (32 RT x 64 INT8) and the packed weights (128 triples x 64)
 //    are copied straight from memory into LDS by buffer loads with the LDS
 //    destination bit (no registers involved), four blocks ahead of use, into
 //    a ring of five LDS slots.  The wait for a block is an explicit vmcnt
@@ -1108,9 +1108,7 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamB
 //
 // Workgroups are mapped XCD-aware and in groups (gemm_tile), so that the
 // tiles resident on one XCD share activation and weight tiles in its L2.
-constexpr int kGemmBM = 128;      // token rows per workgroup
 constexpr int kGemmBF = 8;        // weight fragments (16 triples) per workgroup
-constexpr int kGemmRT = 4;        // 32-row tiles per wave
 constexpr int kGemmSlots = 5;     // LDS ring slots
 constexpr int kGemmAhead = kGemmSlots - 1;  // blocks in flight ahead of use
 constexpr int kXcds = 8;
