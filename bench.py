@@ -4,8 +4,9 @@
 Headline workload: the decode-step GEMV of the Llama-3.2-11B text MLP
 gate/up shape, M=1 token, K=4096, N=14336 (Y = X W^T), S3D8 weights packed
 by the library's packer from N(0, 0.02) fp32 weights, activations N(0,1)
-quantised per token on the GPU.  One step = s3d8_quant_act + s3d8_linear on
-one token, inputs resident in HBM.  The metric is effective weight GB/s:
+quantised per token on the GPU.  One step = s3d8_forward on one token (one
+launch of the streaming GEMV, which quantises the activations in its
+prologue), inputs resident in HBM.  The metric is effective weight GB/s:
 the S3D8 bytes of the matrix (packed bytes + bf16 channel scales + the
 96-byte table) per step time.
 
@@ -16,8 +17,11 @@ are captured once in a HIP graph (R steps, one per copy) and replayed, so
 host launch overhead does not enter the timed region.
 
 Also reported: the prefill GEMM (M=2048, K=4096, N=14336) in INT8 TOPS
-against the INT8 MFMA peak, the dominant kernel's roofline fraction, and the
-CPU oracle timed on the host cores (cpu_baseline).
+against the INT8 MFMA peak, the dominant kernel's roofline fraction, the
+per-call median with a bootstrap interval, measured HBM and INT8 ceilings,
+the decode step at M=4 and 8, the decoder layer, the lm_head decode step,
+the format and output variants, the standalone dequantisation and device
+encoder, and the CPU oracle timed on the host cores (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 Prints one JSON line on stdout; progress goes to stderr.
