@@ -128,8 +128,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build runs the S3D8 linear on a single MI355X "
-              "(see the sharding notes in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the S3D8 linear runs on a single MI355X and has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
