@@ -457,11 +457,124 @@ def test_fit_invariants_gaussian():
     assert cent.min() >= 0 and cent.max() <= 127 * (1 + 2 ** -8)
 
 
-def test_fit_kmeanspp_first_pick_uses_draw_one():
-    """With every vector distinct, the first centre is vector floor(u1 * P)
-    where u1 is the top 53 bits of SplitMix64 draw 1."""
+def test_splitmix64_matches_published_outputs():
+    """The k-means++ draws: SplitMix64 seeded with 0 gives the published first
+    three outputs (the generator's own definition, not the oracle)."""
     g = _golden("splitmix64.json")
     assert [format(oracle.splitmix64(g["seed"], c), "016x") for c in (1, 2, 3)] == g["outputs_hex"]
+
+
+def _u(seed, c):
+    """Uniform draw c in [0, 1): the top 53 bits of SplitMix64 draw c (the
+    generator is pinned against its published outputs above)."""
+    return Fraction(oracle.splitmix64(seed, c) >> 11, 1 << 53)
+
+
+def _points_matrix(cols):
+    """W [3][K] whose triple-0 vectors are the given integer 3-vectors (one per
+    input column).  Every channel holds a 127, so alpha = bf16(127/127) = 1
+    exactly and the normalised vectors W' are the integers themselves."""
+    W = np.array(cols, np.float32).T.copy()
+    assert (W.max(axis=1) == 127).all()
+    return W
+
+
+def _seeded(cols, seed):
+    """The 32 k-means++ centres (no Lloyd iteration), as integer tuples."""
+    W = _points_matrix(cols)
+    _, cent, dist, it = oracle.fit_centroids(W, seed=seed, max_iters=0)
+    assert it == 0
+    assert (cent == np.round(cent)).all()
+    return [tuple(int(v) for v in r) for r in cent], dist
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_kmeanspp_first_pick_is_floor_u1_times_p(seed):
+    """[PAPER] Sec. 3.4 "Quantization": k-means++ draws the first centre
+    uniformly.  With P = 48 distinct vectors, centre 0 is vector
+    floor(u1 * P), u1 = draw 1 (hand rule: the counter-form draw numbering
+    of the fit, pick l uses draw l + 1)."""
+    g = np.random.Generator(np.random.PCG64(970))
+    cols = set()
+    while len(cols) < 47:
+        cols.add(tuple(int(v) for v in g.integers(0, 127, size=3)))
+    cols = [(127, 127, 127)] + sorted(cols)
+    cols = [cols[i] for i in g.permutation(48)]
+    cent, _ = _seeded(cols, seed)
+    first = math.floor(_u(seed, 1) * 48)
+    assert cent[0] == cols[first]
+    # every centre is one of the vectors, and the 32 picks are distinct
+    # (48 distinct vectors: a vector already chosen has D^2 = 0)
+    assert all(c in cols for c in cent) and len(set(cent)) == 32
+
+
+# seeds chosen so that every branch below is taken at least twice
+D2_SEEDS = [7, 14, 3, 4, 19, 25, 1, 2, 0, 13, 22, 31]
+
+
+@pytest.mark.parametrize("seed", D2_SEEDS)
+def test_kmeanspp_d2_pick_hand_worked(seed):
+    """D^2 weighting on four vectors, worked by hand.  a = (127,127,127) twice,
+    b = (127,126,127) and c = (127,127,124): |a-b|^2 = 1, |a-c|^2 = 9,
+    |b-c|^2 = 10.  The first centre is vector floor(4 u1).  Each later pick
+    takes the first vector whose running sum of squared distances to the
+    nearest centre exceeds u * total, so with weights (w0, w1, w2, w3):
+      first a: (0, 0, 1, 9), total 10: b if u2 < 1/10, else c;
+      first b: (1, 1, 0, 10), total 12: a if u2 < 2/12, else c;
+      first c: (9, 9, 10, 0), total 28: a if u2 < 18/28, else b.
+    The third pick is the vector not yet chosen, whatever u3: it is the only
+    one left with a non-zero weight.  Then every weight is 0 and pick l is
+    uniform: vector floor(4 u_{l+1})."""
+    a, b, c = (127, 127, 127), (127, 126, 127), (127, 127, 124)
+    cols = [a, a, b, c]
+    cent, dist = _seeded(cols, seed)
+    u = [None] + [_u(seed, l) for l in range(1, 33)]
+    first = cols[math.floor(4 * u[1])]
+    if first == a:
+        second = b if u[2] < Fraction(1, 10) else c
+    elif first == b:
+        second = a if u[2] < Fraction(2, 12) else c
+    else:
+        second = a if u[2] < Fraction(18, 28) else b
+    third = ({a, b, c} - {first, second}).pop()
+    assert cent[:3] == [first, second, third]
+    for l in range(3, 32):
+        assert cent[l] == cols[math.floor(4 * u[l + 1])], l
+    # every vector coincides with a centre: zero distortion after seeding
+    assert dist[0] == 0.0
+
+
+def test_lloyd_step_hand_worked():
+    """One Lloyd-Max update ([PAPER] Sec. 3.4 "Quantization": assign each
+    vector to its nearest centre, move each centre to the mean of its
+    vectors), worked by hand.  31 grid vectors 42 apart and a cluster of
+    three near (127,127,127): n1 = (127,127,127), n2 = (127,127,125),
+    n3 = (127,125,127) (34 vectors, 32 centres).  For this seed the seeding
+    takes all 31 grid vectors and n1 (the cluster's other two have D^2 <= 8
+    against >= 1600 for any grid vector).  The update moves n1's centre to
+    the cluster mean (127, 379/3, 379/3) and leaves every grid centre (alone
+    in its cell) where it is; the next assignment changes nothing, so the
+    fit stops after one iteration.  Distortion: 4 + 4 = 8 after seeding,
+    then 8/9 + 20/9 + 20/9 = 16/3.  The rounded table row is (127,126,126)."""
+    grid = [(x, y, z) for x in (0, 42, 84, 126) for y in (0, 42, 84, 126) for z in (0, 126)]
+    grid.remove((126, 126, 126))
+    n1, n2, n3 = (127, 127, 127), (127, 127, 125), (127, 125, 127)
+    cols = grid + [n1, n2, n3]
+    seed = 4
+    cent0, dist0 = _seeded(cols, seed)
+    assert set(cent0) == set(grid) | {n1}
+    W = _points_matrix(cols)
+    C, cent, dist, it = oracle.fit_centroids(W, seed=seed, max_iters=5)
+    assert it == 1
+    k = cent0.index(n1)
+    mean = (127.0, 379.0 / 3.0, 379.0 / 3.0)
+    assert tuple(cent[k]) == mean
+    for l, g0 in enumerate(cent0):
+        if l != k:
+            assert tuple(cent[l]) == tuple(float(v) for v in g0)
+    assert dist[0] == 8.0
+    assert dist[1] == pytest.approx(16.0 / 3.0, rel=1e-15)
+    assert tuple(int(v) for v in C[k]) == (127, 126, 126)
 
 
 def test_sign_rule_and_padding_on_encode():
