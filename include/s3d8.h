@@ -82,7 +82,9 @@ int32_t s3d8_version(void);
  * ceil(n/3) rows).  Returns -1 if N <= 0. */
 int64_t s3d8_num_triples(int64_t N);
 
-/* Bytes of the packed index/sign matrix: ceil(N/3) * K.  -1 on bad sizes. */
+/* Bytes of the packed index/sign matrix: ceil(N/3) * K, the ceil(n/3) rows
+ * of k bytes that [PAPER] Eq. 1 indexes (one byte per channel triple and
+ * input column, [BLOG] "Output channel packing").  -1 on bad sizes. */
 int64_t s3d8_packed_bytes(int64_t N, int64_t K);
 
 /* Total storage of one matrix: packed bytes + 2 * 3*ceil(N/3) scale bytes +
@@ -169,16 +171,22 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
  *   xs           device fp32 [M].
  *   tiled        device, the matrix in the tiled layout of s3d8_tile,
  *                16-B aligned.
+ *   tiled_bytes  size of the tiled buffer; at least s3d8_tiled_bytes(N, K).
+ *                A canonical [ceil(N/3)][K] buffer is smaller whenever
+ *                ceil(N/3) is not a multiple of 16 or K not a multiple of
+ *                64, and is then rejected (INVALID_ARG) instead of being
+ *                misread; at other shapes the two layouts have the same
+ *                size and only the caller can tell them apart.
  *   centroids    device uint8 [32][3], 4-B aligned.
  *   scales_bf16  device uint16 [3*ceil(N/3)] (entries >= N are not read).
  *   y            out, device fp32 [M][N], row-major.
  *   acc_out      optional out (NULL to skip), device int32 [M][N]: the
  *                accumulators before the epilogue, for verification.
- * Errors: INVALID_ARG, SHAPE (also N > 3355442 when M > 16), ALIGN, DEVICE,
- * HIP. */
+ * Errors: INVALID_ARG (also tiled_bytes too small), SHAPE (also N > 3355442
+ * when M > 16), ALIGN, DEVICE, HIP. */
 int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
-                    float *y, int32_t *acc_out, void *stream);
+                    const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                    const uint16_t *scales_bf16, float *y, int32_t *acc_out, void *stream);
 
 /* The whole path from fp32 activations: per-token INT8 quantisation (as
  * s3d8_quant_act) followed by the fused linear (as s3d8_linear).  For M <= 4
@@ -186,19 +194,21 @@ int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int
  * s3d8_quant_act and s3d8_linear are enqueued in turn.  Results are
  * identical to calling the two entry points.
  *   x            device fp32 [M][K], 16-B aligned, finite.
- *   tiled, centroids, scales_bf16, y, acc_out   as for s3d8_linear.
+ *   tiled, tiled_bytes, centroids, scales_bf16, y, acc_out
+ *                as for s3d8_linear.
  *   xq           out, device int8 [M][K], 16-B aligned: the activation codes.
  *   xs           out, device fp32 [M]: the activation scales.
  * Errors: INVALID_ARG, SHAPE, ALIGN, DEVICE, HIP. */
 int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                     const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq,
-                     float *xs, int32_t *acc_out, void *stream);
+                     int64_t tiled_bytes, const uint8_t *centroids, const uint16_t *scales_bf16,
+                     float *y, int8_t *xq, float *xs, int32_t *acc_out, void *stream);
 
 /* One item of s3d8_forward_batch: the arguments of one s3d8_forward call. */
 typedef struct s3d8_forward_item {
     const float *x;               /* device fp32 [M][K], 16-B aligned, finite */
     int64_t M, K, N;
     const uint8_t *tiled;         /* as for s3d8_linear */
+    int64_t tiled_bytes;          /* as for s3d8_linear */
     const uint8_t *centroids;     /* as for s3d8_linear */
     const uint16_t *scales_bf16;  /* as for s3d8_linear */
     float *y;                     /* out, device fp32 [M][N] */
@@ -252,19 +262,19 @@ int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K);
  * identical to s3d8_linear; for many token rows it decodes each weight once
  * per call instead of once per row tile.  (The workspace layout is
  * internal to the library.)
- *   xq, xs, M, K, N, tiled, centroids, scales_bf16, y, acc_out
+ *   xq, xs, M, K, N, tiled, tiled_bytes, centroids, scales_bf16, y, acc_out
  *                as for s3d8_linear.
  *   workspace    device scratch, 16-B aligned, at least
  *                s3d8_unfused_workspace_bytes(N, K) bytes, owned by the
  *                caller; overwritten.  Calls that may run concurrently
  *                need separate workspaces.
  *   workspace_bytes  its size.
- * Errors: INVALID_ARG (also a workspace too small), SHAPE (decoded matrix
+ * Errors: INVALID_ARG (also a workspace or tiled_bytes too small), SHAPE (decoded matrix
  * over 2^31 bytes, or N > 3355442), ALIGN, DEVICE, HIP. */
 int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
-                            float *y, int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes,
-                            void *stream);
+                            const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                            const uint16_t *scales_bf16, float *y, int32_t *acc_out, int8_t *workspace,
+                            int64_t workspace_bytes, void *stream);
 
 /* Decode a whole matrix to channel-INT8 ([PAPER] Eq. 1 without alpha; the
  * blog's standalone S3D8 -> INT8 dequantisation).
@@ -312,25 +322,25 @@ int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N,
  * Errors: as s3d8_linear; INVALID_ARG also for an unknown format or output
  * type.  With S3D8_FORMAT_S3D8 and S3D8_OUT_F32 it is s3d8_linear. */
 int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                       const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
-                       int32_t *acc_out, void *stream);
+                       int64_t tiled_bytes, const void *table, int32_t format, const uint16_t *scales_bf16, void *y,
+                       int32_t out_type, int32_t *acc_out, void *stream);
 
 /* s3d8_forward for either weight format and either output type (arguments
  * as s3d8_linear_ex and s3d8_forward; xq and xs as for s3d8_forward).  The
  * same launches as s3d8_forward.  Errors: as s3d8_forward, plus
  * INVALID_ARG for an unknown format or output type. */
-int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
-                        int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type, int8_t *xq, float *xs,
-                        int32_t *acc_out, void *stream);
+int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_bytes,
+                        const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
+                        int8_t *xq, float *xs, int32_t *acc_out, void *stream);
 
 /* s3d8_linear_unfused for either weight format and either output type
  * (arguments as s3d8_linear_ex, workspace as s3d8_linear_unfused).
  * Errors: as s3d8_linear_unfused, plus INVALID_ARG for an unknown format or
  * output type. */
 int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                               const uint8_t *tiled, const void *table, int32_t format, const uint16_t *scales_bf16,
-                               void *y, int32_t out_type, int32_t *acc_out, int8_t *workspace,
-                               int64_t workspace_bytes, void *stream);
+                               const uint8_t *tiled, int64_t tiled_bytes, const void *table, int32_t format,
+                               const uint16_t *scales_bf16, void *y, int32_t out_type, int32_t *acc_out,
+                               int8_t *workspace, int64_t workspace_bytes, void *stream);
 
 /* s3d8_dequant for either weight format: w = the table decode of every
  * byte, channel-INT8 [N][K] (padded channels not written).  table and
@@ -351,6 +361,19 @@ int32_t s3d8_dequant_ex(const uint8_t *packed, const void *table, int32_t format
  * Errors: INVALID_ARG (out NULL, iters < 1, workgroups outside
  * [1, 65536], v outside [-128, 127]), ALIGN, DEVICE, HIP. */
 int32_t s3d8_mfma_rate_probe(int32_t iters, int32_t workgroups, int32_t v, int32_t *out, void *stream);
+
+/* Memory read probe: a measurement utility for reading the memory-bound
+ * kernels against the rate at which a buffer of the same size streams out of
+ * device memory, not part of the method.  `workgroups` workgroups of 256
+ * threads read the `bytes` bytes at p as 16-byte chunks (chunk c by
+ * workgroup (c / 256) mod workgroups) and workgroup w stores the XOR of the
+ * 32-bit words it read to out[w]; the XOR of all of out is therefore the
+ * XOR of all words of p.
+ *   p      device, 16-B aligned; bytes a positive multiple of 16.
+ *   out    out, device uint32 [workgroups], 4-B aligned.
+ * Errors: INVALID_ARG (null pointer, bytes not a positive multiple of 16,
+ * workgroups outside [1, 65536]), ALIGN, DEVICE, HIP. */
+int32_t s3d8_hbm_read_probe(const void *p, int64_t bytes, int32_t workgroups, uint32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

@@ -74,12 +74,15 @@ def test_quant_act_validation():
     assert _err("s3d8_quant_act", A_ODD, 1, 16, A16, A16, None)[0] == _lib.S3D8_ERR_ALIGN
 
 
+TB = 1 << 40  # a tiled_bytes large enough for every shape below
+
+
 def test_linear_validation():
-    good = dict(xq=A16, xs=A16, M=1, K=64, N=9, packed=A16, C=A16, s=A16, y=A16, acc=None)
+    good = dict(xq=A16, xs=A16, M=1, K=64, N=9, packed=A16, tb=TB, C=A16, s=A16, y=A16, acc=None)
 
     def call(**kw):
         a = dict(good, **kw)
-        return _err("s3d8_linear", a["xq"], a["xs"], a["M"], a["K"], a["N"], a["packed"], a["C"],
+        return _err("s3d8_linear", a["xq"], a["xs"], a["M"], a["K"], a["N"], a["packed"], a["tb"], a["C"],
                     a["s"], a["y"], a["acc"], None)[0]
 
     assert call(xq=None) == _lib.S3D8_ERR_INVALID_ARG
@@ -95,6 +98,43 @@ def test_linear_validation():
     assert call(N=1 << 30, K=1 << 12) == _lib.S3D8_ERR_SHAPE
 
 
+@pytest.mark.parametrize("entry", ["s3d8_linear", "s3d8_forward", "s3d8_linear_unfused", "s3d8_linear_ex",
+                                   "s3d8_forward_ex", "s3d8_linear_unfused_ex", "s3d8_forward_batch"])
+def test_canonical_buffer_rejected_as_tiled(entry):
+    """A buffer of the canonical packed size ceil(N/3) * K passed where the
+    tiled layout is expected is refused (INVALID_ARG) before any GPU work:
+    at c1 (N = 14336, K = 4096) the canonical matrix is 19,574,784 bytes and
+    the tiled one 19,595,264."""
+    L = _lib.lib()
+    N, K = 14336, 4096
+    canon, tiled = L.s3d8_packed_bytes(N, K), L.s3d8_tiled_bytes(N, K)
+    assert canon < tiled
+    ws = L.s3d8_unfused_workspace_bytes(N, K)
+
+    def call(tb):
+        if entry == "s3d8_linear":
+            return L.s3d8_linear(A16, A16, 1, K, N, A16, tb, A16, A16, A16, None, None)
+        if entry == "s3d8_forward":
+            return L.s3d8_forward(A16, 1, K, N, A16, tb, A16, A16, A16, A16, A16, None, None)
+        if entry == "s3d8_linear_unfused":
+            return L.s3d8_linear_unfused(A16, A16, 40, K, N, A16, tb, A16, A16, A16, None, A16, ws, None)
+        if entry == "s3d8_linear_ex":
+            return L.s3d8_linear_ex(A16, A16, 1, K, N, A16, tb, A16, 1, A16, A16, 1, None, None)
+        if entry == "s3d8_forward_ex":
+            return L.s3d8_forward_ex(A16, 1, K, N, A16, tb, A16, 1, A16, A16, 1, A16, A16, None, None)
+        if entry == "s3d8_linear_unfused_ex":
+            return L.s3d8_linear_unfused_ex(A16, A16, 40, K, N, A16, tb, A16, 0, A16, A16, 1, None, A16, ws, None)
+        item = _lib.ForwardItem(x=A16, M=1, K=K, N=N, tiled=A16, tiled_bytes=tb, centroids=A16, scales_bf16=A16,
+                                y=A16, xq=A16, xs=A16, acc_out=None)
+        items = (_lib.ForwardItem * 1)(item)
+        return L.s3d8_forward_batch(1, ctypes.addressof(items), None)
+
+    assert call(canon) == _lib.S3D8_ERR_INVALID_ARG
+    assert "tiled" in L.s3d8_last_error().decode()
+    assert call(tiled - 1) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(0) == _lib.S3D8_ERR_INVALID_ARG
+
+
 def test_tile_and_forward_validation():
     L = _lib.lib()
     assert L.s3d8_tiled_bytes(14336, 4096) == 299 * 64 * 1024
@@ -106,9 +146,9 @@ def test_tile_and_forward_validation():
     assert L.s3d8_tile(A16, 1 << 31, 4096, A16, None) == _lib.S3D8_ERR_SHAPE
 
     def fwd(**kw):
-        a = dict(x=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, xq=A16, xs=A16, acc=None)
+        a = dict(x=A16, M=1, K=64, N=9, t=A16, tb=TB, C=A16, s=A16, y=A16, xq=A16, xs=A16, acc=None)
         a.update(kw)
-        return L.s3d8_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["C"], a["s"], a["y"], a["xq"],
+        return L.s3d8_forward(a["x"], a["M"], a["K"], a["N"], a["t"], a["tb"], a["C"], a["s"], a["y"], a["xq"],
                               a["xs"], a["acc"], None)
 
     assert fwd(x=None) == _lib.S3D8_ERR_INVALID_ARG
@@ -127,6 +167,18 @@ def test_dequant_validation():
     assert L.s3d8_dequant(A16, A16, 3, 16, A_ODD, None) == _lib.S3D8_ERR_ALIGN
     assert L.s3d8_dequant(A16, A16 + 1, 3, 16, A16, None) == _lib.S3D8_ERR_ALIGN
     assert L.s3d8_dequant(A16, A16, 0, 16, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+
+
+def test_hbm_read_probe_validation():
+    L = _lib.lib()
+    assert L.s3d8_hbm_read_probe(None, 16, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A16, 16, 1, None, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A16, 0, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A16, 24, 1, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A16, 16, 0, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A16, 16, 65537, A16, None) == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_hbm_read_probe(A_ODD, 16, 1, A16, None) == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_hbm_read_probe(A16, 16, 1, A16 + 2, None) == _lib.S3D8_ERR_ALIGN
 
 
 def test_mfma_rate_probe_validation():
@@ -148,7 +200,7 @@ def test_linear_unfused_validation():
     need = L.s3d8_unfused_workspace_bytes(9, 64)
 
     def call(ws=A16, nbytes=need, xq=A16, K=64):
-        return L.s3d8_linear_unfused(xq, A16, 1, K, 9, A16, A16, A16, A16, None, ws, nbytes, None)
+        return L.s3d8_linear_unfused(xq, A16, 1, K, 9, A16, TB, A16, A16, A16, None, ws, nbytes, None)
 
     assert call(ws=None) == _lib.S3D8_ERR_INVALID_ARG
     assert call(nbytes=need - 1) == _lib.S3D8_ERR_INVALID_ARG
@@ -158,7 +210,7 @@ def test_linear_unfused_validation():
     assert call(nbytes=need - 1) == _lib.S3D8_ERR_INVALID_ARG
     assert b"workspace" in L.s3d8_last_error()
     # a decoded matrix over 2^31 bytes is refused before any device work
-    assert L.s3d8_linear_unfused(A16, A16, 1, 16384, 400000, A16, A16, A16, A16, None, A16, 1 << 40,
+    assert L.s3d8_linear_unfused(A16, A16, 1, 16384, 400000, A16, TB, A16, A16, A16, None, A16, 1 << 40,
                                  None) == _lib.S3D8_ERR_SHAPE
 
 
@@ -167,8 +219,8 @@ def test_forward_batch_validation():
     assert L.s3d8_forward_batch(0, None, None) == 0  # nothing to do, no device touched
     assert L.s3d8_forward_batch(-1, None, None) == _lib.S3D8_ERR_INVALID_ARG
     assert L.s3d8_forward_batch(1, None, None) == _lib.S3D8_ERR_INVALID_ARG
-    good = dict(x=A16, M=1, K=64, N=9, tiled=A16, centroids=A16, scales_bf16=A16, y=A16, xq=A16, xs=A16,
-                acc_out=None)
+    good = dict(x=A16, M=1, K=64, N=9, tiled=A16, tiled_bytes=TB, centroids=A16, scales_bf16=A16, y=A16, xq=A16,
+                xs=A16, acc_out=None)
 
     def call(**kw):
         items = (_lib.ForwardItem * 2)(_lib.ForwardItem(**good), _lib.ForwardItem(**dict(good, **kw)))
@@ -179,7 +231,8 @@ def test_forward_batch_validation():
     assert call(K=40) == _lib.S3D8_ERR_SHAPE
     assert call(x=A_ODD) == _lib.S3D8_ERR_ALIGN
     assert call(tiled=A_ODD) == _lib.S3D8_ERR_ALIGN
-    assert ctypes.sizeof(_lib.ForwardItem) == 88
+    assert call(tiled_bytes=0) == _lib.S3D8_ERR_INVALID_ARG
+    assert ctypes.sizeof(_lib.ForwardItem) == 96
 
 
 def test_encode_device_validation():
@@ -233,8 +286,8 @@ def test_variant_entry_points_validation():
     def lin(fmt=0, out=0, **kw):
         a = dict(xq=A16, xs=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, acc=None)
         a.update(kw)
-        return L.s3d8_linear_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"], a["y"],
-                                out, a["acc"], None)
+        return L.s3d8_linear_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], TB, a["C"], fmt, a["s"],
+                                a["y"], out, a["acc"], None)
 
     assert lin(fmt=2) == _lib.S3D8_ERR_INVALID_ARG
     assert lin(fmt=-1) == _lib.S3D8_ERR_INVALID_ARG
@@ -248,7 +301,7 @@ def test_variant_entry_points_validation():
     def fwd(fmt=0, out=0, **kw):
         a = dict(x=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, xq=A16, xs=A16, acc=None)
         a.update(kw)
-        return L.s3d8_forward_ex(a["x"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"], a["y"], out,
+        return L.s3d8_forward_ex(a["x"], a["M"], a["K"], a["N"], a["t"], TB, a["C"], fmt, a["s"], a["y"], out,
                                  a["xq"], a["xs"], a["acc"], None)
 
     assert fwd(fmt=7) == _lib.S3D8_ERR_INVALID_ARG
@@ -260,8 +313,8 @@ def test_variant_entry_points_validation():
     def unf(fmt=0, out=0, **kw):
         a = dict(xq=A16, xs=A16, M=1, K=64, N=9, t=A16, C=A16, s=A16, y=A16, acc=None, ws=A16, wb=1 << 20)
         a.update(kw)
-        return L.s3d8_linear_unfused_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], a["C"], fmt, a["s"],
-                                        a["y"], out, a["acc"], a["ws"], a["wb"], None)
+        return L.s3d8_linear_unfused_ex(a["xq"], a["xs"], a["M"], a["K"], a["N"], a["t"], TB, a["C"], fmt,
+                                        a["s"], a["y"], out, a["acc"], a["ws"], a["wb"], None)
 
     assert unf(fmt=3) == _lib.S3D8_ERR_INVALID_ARG
     assert unf(out=5) == _lib.S3D8_ERR_INVALID_ARG

@@ -6,9 +6,9 @@ where the oracle's output is zero).  The epilogue is two fp32 multiplies in a
 fixed order, so the outputs are also expected to be bit-identical; that is
 checked too.
 
-Small shapes are compared element by element over whole outputs; full-size
-workloads are compared in full where the oracle finishes in seconds, and on
-sampled outputs (each computed by the oracle one by one) otherwise.
+Small shapes are compared element by element over whole outputs; so are the
+full-size decode workloads here and the full-size prefill workloads in
+test_gpu_full_prefill.py.
 """
 import numpy as np
 import pytest
@@ -208,27 +208,6 @@ def _full_compare(lin, gpu, M=None):
     check_y(y, y_r)
 
 
-def _sampled_compare(lin, gpu, nsamples=512, unfused=False):
-    C, alpha, packed = packed_matrix(lin)
-    x = workloads.activations(lin)
-    xq, xs, acc, y = run_linear(x, C, alpha, packed, lin.N, gpu, unfused=unfused)
-    xq_r, xs_r = oracle.quant_act(x)
-    np.testing.assert_array_equal(xq, xq_r)
-    np.testing.assert_array_equal(xs, xs_r)
-    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2040, lin.config_id, lin.matrix_id])))
-    ms = list(g.integers(0, lin.M, nsamples)) + [0, lin.M - 1, 0, lin.M - 1]
-    ns = list(g.integers(0, lin.N, nsamples)) + [0, 0, lin.N - 1, lin.N - 1]
-    ref = np.array([oracle.acc_one(xq_r[m], packed, C, lin.K, n) for m, n in zip(ms, ns)], np.int64)
-    got = acc[np.array(ms), np.array(ns)].astype(np.int64)
-    np.testing.assert_array_equal(got, ref)
-    acc_s = ref.astype(np.int32).reshape(-1, 1)
-    for i, (m, n) in enumerate(zip(ms, ns)):
-        y_r = oracle.epilogue(acc_s[i:i + 1], xs_r[m:m + 1], alpha[n:n + 1], 1)
-        check_y(y[m, n:n + 1].reshape(1, 1), y_r)
-    # the whole output is finite and padded channels never leak in
-    assert y.shape == (lin.M, lin.N) and np.isfinite(y).all()
-
-
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_linear_gate_up_decode(gpu, m):
     _full_compare(workloads.C1[m], gpu)
@@ -241,15 +220,6 @@ def test_linear_decoder_layer(gpu, idx):
 
 def test_linear_lm_head_decode(gpu):
     _full_compare(workloads.C4[0], gpu)
-
-
-def test_linear_prefill_gemm_sampled(gpu):
-    _sampled_compare(workloads.C3, gpu)
-
-
-@pytest.mark.parametrize("idx", [1, 2, 3])
-def test_linear_prefill_c4_sampled(gpu, idx):
-    _sampled_compare(workloads.C4[idx], gpu)
 
 
 def test_linear_prefill_five_row_tiles(gpu):
@@ -506,15 +476,6 @@ def test_linear_unfused_extremes_and_zeros(gpu):
     assert acc.tolist() == [[big] * 3 + [-big] * 3, [-big] * 3 + [big] * 3, [0] * 6]
     _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
     check_y(y, y_r)
-
-
-def test_linear_unfused_prefill_gemm_sampled(gpu):
-    _sampled_compare(workloads.C3, gpu, unfused=True)
-
-
-@pytest.mark.parametrize("idx", [1, 2, 3])
-def test_linear_unfused_prefill_c4_sampled(gpu, idx):
-    _sampled_compare(workloads.C4[idx], gpu, unfused=True)
 
 
 def test_linear_unfused_matches_fused_full(gpu):

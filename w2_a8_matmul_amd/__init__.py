@@ -24,7 +24,7 @@ from ._lib import S3D8Error, call, lib  # noqa: F401
 __all__ = [
     "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "tiled_bytes", "pack", "encode",
     "tile", "quant_act", "linear", "linear_unfused", "unfused_workspace_bytes", "forward", "dequant",
-    "PackedLinear",
+    "PackedLinear", "hbm_read_probe", "mfma_rate_probe", "encode_device", "forward_batch",
 ]
 
 
@@ -94,7 +94,11 @@ def _stream(t) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
-def _dev_check(t, dtype, name):
+def _dev_check(t, dtype, name, device=None, numel=None, min_numel=None):
+    """A device tensor argument: torch tensor on the GPU (on `device` when
+    given), of `dtype`, contiguous, and with exactly `numel` (or at least
+    `min_numel`) elements when given.  Outputs are checked with numel, so the
+    kernels never write past a caller-supplied buffer."""
     torch = _torch()
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise TypeError(f"{name} must be a CUDA/HIP torch tensor")
@@ -102,6 +106,12 @@ def _dev_check(t, dtype, name):
         raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, got {t.numel()}")
 
 
 def quant_act(x, xq=None, xs=None):
@@ -109,10 +119,7 @@ def quant_act(x, xq=None, xs=None):
     torch = _torch()
     _dev_check(x, torch.float32, "x")
     M, K = x.shape
-    if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if xs is None:
-        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
+    xq, xs = _codes_out(xq, xs, M, K, x.device)
     with torch.cuda.device(x.device):
         call("s3d8_quant_act", x.data_ptr(), M, K, xq.data_ptr(), xs.data_ptr(), _stream(x))
     return xq, xs
@@ -128,6 +135,7 @@ def tile(packed, N: int, tiled=None):
         raise ValueError("packed rows do not match N")
     if tiled is None:
         tiled = torch.empty((tiled_bytes(N, K),), dtype=torch.uint8, device=packed.device)
+    _dev_check(tiled, torch.uint8, "tiled", packed.device, min_numel=tiled_bytes(N, K))
     with torch.cuda.device(packed.device):
         call("s3d8_tile", packed.data_ptr(), N, K, tiled.data_ptr(), _stream(packed))
     return tiled
@@ -162,18 +170,45 @@ def _table_view(table, fmt: str):
     return table
 
 
-def _check_weights(tiled, centroids, scales, N, K, fmt: str = "s3d8"):
+def _check_weights(tiled, centroids, scales, N, K, fmt: str = "s3d8", device=None):
     torch = _torch()
-    _dev_check(tiled, torch.uint8, "tiled")
-    _table_view(centroids, fmt)
+    _dev_check(tiled, torch.uint8, "tiled", device)
+    table = _table_view(centroids, fmt)
+    _dev_check(table, torch.uint8, "centroids", device)
+    _dev_check(scales, torch.int16, "scales", device)
     T = num_triples(N)
     if tiled.numel() < tiled_bytes(N, K) or scales.numel() < 3 * T:
         raise ValueError("tiled / centroids / scales do not match (N, K)")
 
 
-def _new_y(M, N, out, device):
+def _y_out(y, M, N, out, device):
+    """The output buffer: a new one, or a caller's of the right type and size."""
     torch = _torch()
-    return torch.empty((M, N), dtype=torch.float32 if out == "f32" else torch.bfloat16, device=device)
+    dtype = torch.float32 if out == "f32" else torch.bfloat16
+    if y is None:
+        return torch.empty((M, N), dtype=dtype, device=device)
+    _dev_check(y, dtype, "y", device, numel=M * N)
+    return y
+
+
+def _acc_out(acc, want, M, N, device):
+    torch = _torch()
+    if acc is None:
+        return torch.empty((M, N), dtype=torch.int32, device=device) if want else None
+    _dev_check(acc, torch.int32, "acc", device, numel=M * N)
+    return acc
+
+
+def _codes_out(xq, xs, M, K, device):
+    """Activation codes and scales written by quant_act / forward."""
+    torch = _torch()
+    if xq is None:
+        xq = torch.empty((M, K), dtype=torch.int8, device=device)
+    if xs is None:
+        xs = torch.empty((M,), dtype=torch.float32, device=device)
+    _dev_check(xq, torch.int8, "xq", device, numel=M * K)
+    _dev_check(xs, torch.float32, "xs", device, numel=M)
+    return xq, xs
 
 
 def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_acc: bool = False,
@@ -183,16 +218,14 @@ def linear(xq, xs, tiled, centroids, scales, N: int, y=None, acc=None, return_ac
     torch = _torch()
     f, o = _variant(fmt, out)
     _dev_check(xq, torch.int8, "xq")
-    _dev_check(xs, torch.float32, "xs")
-    scales = _scales_view(scales)
     M, K = xq.shape
-    _check_weights(tiled, centroids, scales, N, K, fmt)
-    if y is None:
-        y = _new_y(M, N, out, xq.device)
-    if return_acc and acc is None:
-        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _dev_check(xs, torch.float32, "xs", xq.device, min_numel=M)
+    scales = _scales_view(scales)
+    _check_weights(tiled, centroids, scales, N, K, fmt, xq.device)
+    y = _y_out(y, M, N, out, xq.device)
+    acc = _acc_out(acc, return_acc, M, N, xq.device)
     with torch.cuda.device(xq.device):
-        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr())
+        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), tiled.numel(), centroids.data_ptr())
         tail = (acc.data_ptr() if acc is not None else None, _stream(xq))
         if f == 0 and o == 0:
             call("s3d8_linear", *args, scales.data_ptr(), y.data_ptr(), *tail)
@@ -214,20 +247,18 @@ def linear_unfused(xq, xs, tiled, centroids, scales, N: int, workspace=None, y=N
     torch = _torch()
     f, o = _variant(fmt, out)
     _dev_check(xq, torch.int8, "xq")
-    _dev_check(xs, torch.float32, "xs")
-    scales = _scales_view(scales)
     M, K = xq.shape
-    _check_weights(tiled, centroids, scales, N, K, fmt)
+    _dev_check(xs, torch.float32, "xs", xq.device, min_numel=M)
+    scales = _scales_view(scales)
+    _check_weights(tiled, centroids, scales, N, K, fmt, xq.device)
     wbytes = unfused_workspace_bytes(N, K)
     if workspace is None:
         workspace = torch.empty((wbytes,), dtype=torch.int8, device=xq.device)
-    _dev_check(workspace, torch.int8, "workspace")
-    if y is None:
-        y = _new_y(M, N, out, xq.device)
-    if return_acc and acc is None:
-        acc = torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _dev_check(workspace, torch.int8, "workspace", xq.device, min_numel=wbytes)
+    y = _y_out(y, M, N, out, xq.device)
+    acc = _acc_out(acc, return_acc, M, N, xq.device)
     with torch.cuda.device(xq.device):
-        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr())
+        args = (xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), tiled.numel(), centroids.data_ptr())
         tail = (acc.data_ptr() if acc is not None else None, workspace.data_ptr(), workspace.numel(),
                 _stream(xq))
         if f == 0 and o == 0:
@@ -249,23 +280,18 @@ def forward(x, tiled, centroids, scales, N: int, y=None, xq=None, xs=None, acc=N
     _dev_check(x, torch.float32, "x")
     scales = _scales_view(scales)
     M, K = x.shape
-    _check_weights(tiled, centroids, scales, N, K, fmt)
-    if y is None:
-        y = _new_y(M, N, out, x.device)
-    if xq is None:
-        xq = torch.empty((M, K), dtype=torch.int8, device=x.device)
-    if xs is None:
-        xs = torch.empty((M,), dtype=torch.float32, device=x.device)
-    if return_all and acc is None:
-        acc = torch.empty((M, N), dtype=torch.int32, device=x.device)
+    _check_weights(tiled, centroids, scales, N, K, fmt, x.device)
+    y = _y_out(y, M, N, out, x.device)
+    xq, xs = _codes_out(xq, xs, M, K, x.device)
+    acc = _acc_out(acc, return_all, M, N, x.device)
     with torch.cuda.device(x.device):
         tail = (xq.data_ptr(), xs.data_ptr(), acc.data_ptr() if acc is not None else None, _stream(x))
         if f == 0 and o == 0:
-            call("s3d8_forward", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(),
+            call("s3d8_forward", x.data_ptr(), M, K, N, tiled.data_ptr(), tiled.numel(), centroids.data_ptr(),
                  scales.data_ptr(), y.data_ptr(), *tail)
         else:
-            call("s3d8_forward_ex", x.data_ptr(), M, K, N, tiled.data_ptr(), centroids.data_ptr(), f,
-                 scales.data_ptr(), y.data_ptr(), o, *tail)
+            call("s3d8_forward_ex", x.data_ptr(), M, K, N, tiled.data_ptr(), tiled.numel(), centroids.data_ptr(),
+                 f, scales.data_ptr(), y.data_ptr(), o, *tail)
     if return_all:
         return y, xq, xs, acc
     return y
@@ -287,23 +313,17 @@ def forward_batch(items, return_all: bool = False):
         scales = _scales_view(it["scales"])
         M, K = x.shape
         N = int(it["N"])
-        _check_weights(it["tiled"], it["centroids"], scales, N, K)
         if dev is None:
             dev = x.device
         elif x.device != dev:
             raise ValueError("all items must be on one device")
-        y = it.get("y")
-        y = torch.empty((M, N), dtype=torch.float32, device=dev) if y is None else y
-        xq = it.get("xq")
-        xq = torch.empty((M, K), dtype=torch.int8, device=dev) if xq is None else xq
-        xs = it.get("xs")
-        xs = torch.empty((M,), dtype=torch.float32, device=dev) if xs is None else xs
-        acc = it.get("acc")
-        if return_all and acc is None:
-            acc = torch.empty((M, N), dtype=torch.int32, device=dev)
-        arr[i] = _lib.ForwardItem(x.data_ptr(), M, K, N, it["tiled"].data_ptr(), it["centroids"].data_ptr(),
-                                  scales.data_ptr(), y.data_ptr(), xq.data_ptr(), xs.data_ptr(),
-                                  acc.data_ptr() if acc is not None else None)
+        _check_weights(it["tiled"], it["centroids"], scales, N, K, device=dev)
+        y = _y_out(it.get("y"), M, N, "f32", dev)
+        xq, xs = _codes_out(it.get("xq"), it.get("xs"), M, K, dev)
+        acc = _acc_out(it.get("acc"), return_all, M, N, dev)
+        arr[i] = _lib.ForwardItem(x.data_ptr(), M, K, N, it["tiled"].data_ptr(), it["tiled"].numel(),
+                                  it["centroids"].data_ptr(), scales.data_ptr(), y.data_ptr(), xq.data_ptr(),
+                                  xs.data_ptr(), acc.data_ptr() if acc is not None else None)
         outs.append((y, xq, xs, acc, x, scales))
     if items:
         with torch.cuda.device(dev):
@@ -340,6 +360,8 @@ def dequant(packed, centroids, N: int, w=None, fmt: str = "s3d8"):
         raise ValueError("packed rows do not match N")
     if w is None:
         w = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _dev_check(centroids, torch.uint8, "centroids", packed.device)
+    _dev_check(w, torch.int8, "w", packed.device, numel=N * K)
     with torch.cuda.device(packed.device):
         if f == 0:
             call("s3d8_dequant", packed.data_ptr(), centroids.data_ptr(), N, K, w.data_ptr(), _stream(packed))
@@ -363,6 +385,23 @@ def mfma_rate_probe(iters: int, workgroups: int, v: int = 1, out=None, device="c
     with torch.cuda.device(out.device):
         call("s3d8_mfma_rate_probe", iters, workgroups, v, out.data_ptr(), _stream(out))
     return out, workgroups * 4 * 4 * iters * 65536
+
+
+def hbm_read_probe(buf, workgroups: int, out=None):
+    """Memory read probe (a measurement utility): `workgroups` workgroups of
+    256 threads stream the bytes of the device tensor `buf` (a multiple of 16
+    bytes) and workgroup w stores the XOR of the 32-bit words it read into
+    out[w] (uint32 as int32 [workgroups]).  Returns out."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA/HIP torch tensor")
+    if out is None:
+        out = torch.empty((workgroups,), dtype=torch.int32, device=buf.device)
+    _dev_check(out, torch.int32, "out", buf.device, min_numel=workgroups)
+    nbytes = buf.numel() * buf.element_size()
+    with torch.cuda.device(buf.device):
+        call("s3d8_hbm_read_probe", buf.data_ptr(), nbytes, workgroups, out.data_ptr(), _stream(buf))
+    return out
 
 
 class PackedLinear:

@@ -35,25 +35,26 @@ SIGNATURES = {
     "s3d8_quant_act": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "s3d8_tiled_bytes": (_I64, [_I64, _I64]),
     "s3d8_tile": (_I32, [_P, _I64, _I64, _P, _P]),
-    "s3d8_linear": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
-    "s3d8_forward": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "s3d8_linear": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P]),
+    "s3d8_forward": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "s3d8_dequant": (_I32, [_P, _P, _I64, _I64, _P, _P]),
     "s3d8_unfused_workspace_bytes": (_I64, [_I64, _I64]),
-    "s3d8_linear_unfused": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _I64, _P]),
+    "s3d8_linear_unfused": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P, _I64, _P]),
     "s3d8_forward_batch": (_I32, [_I32, _P, _P]),
     "s3d8_encode_device": (_I32, [_P, _I64, _I64, _P, _P, _P, _P]),
-    "s3d8_linear_ex": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P]),
-    "s3d8_forward_ex": (_I32, [_P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P, _P, _P]),
-    "s3d8_linear_unfused_ex": (_I32, [_P, _P, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P]),
+    "s3d8_linear_ex": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _I32, _P, _P]),
+    "s3d8_forward_ex": (_I32, [_P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _I32, _P, _P, _P, _P]),
+    "s3d8_linear_unfused_ex": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _I32, _P, _P, _I64, _P]),
     "s3d8_dequant_ex": (_I32, [_P, _P, _I32, _I64, _I64, _P, _P]),
     "s3d8_mfma_rate_probe": (_I32, [_I32, _I32, _I32, _P, _P]),
+    "s3d8_hbm_read_probe": (_I32, [_P, _I64, _I32, _P, _P]),
 }
 
 
 class ForwardItem(ctypes.Structure):
     """s3d8_forward_item of include/s3d8.h (all members 8 bytes wide)."""
-    _fields_ = [("x", _P), ("M", _I64), ("K", _I64), ("N", _I64), ("tiled", _P), ("centroids", _P),
-                ("scales_bf16", _P), ("y", _P), ("xq", _P), ("xs", _P), ("acc_out", _P)]
+    _fields_ = [("x", _P), ("M", _I64), ("K", _I64), ("N", _I64), ("tiled", _P), ("tiled_bytes", _I64),
+                ("centroids", _P), ("scales_bf16", _P), ("y", _P), ("xq", _P), ("xs", _P), ("acc_out", _P)]
 
 _lib = None
 

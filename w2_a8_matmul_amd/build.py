@@ -5,6 +5,7 @@ from __future__ import annotations
 import os
 import shutil
 import subprocess
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -31,10 +32,21 @@ HOST_FLAGS = ["-O3", "-fPIC", "-std=c++17", "-march=x86-64-v3", "-ffp-contract=o
               "-fno-fast-math", "-pthread", "-I", INCLUDE, "-I", CSRC]
 
 
+# hipcc hands the target feature above to its host (x86) pass as well, which
+# ignores it with this note; the feature is meant for the device pass only and
+# the driver offers no device-only form of -Xclang, so the note is dropped
+_HOST_PASS_NOTE = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    r = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    err = "".join(line for line in r.stderr.splitlines(keepends=True) if _HOST_PASS_NOTE not in line)
+    if err:
+        print(err, end="", file=sys.stderr, flush=True)
+    if r.returncode != 0:
+        raise subprocess.CalledProcessError(r.returncode, cmd)
 
 
 def build(verbose: bool = False) -> str:

@@ -1544,6 +1544,36 @@ __global__ __launch_bounds__(kRateThreads) void mfma_rate_kernel(int iters, int 
     out[(int64_t)blockIdx.x * kRateThreads + threadIdx.x] = (int32_t)sum;
 }
 
+// --------------------------------------------------------------- HBM read probe
+
+// A measurement utility, not part of the method: how fast the chip streams a
+// buffer of a given size out of memory, the ceiling a memory-bound kernel of
+// that size is read against (the decode GEMV reads 19.6 MB per call, a size
+// at which start-up and drain weigh as much as the bandwidth).  Workgroup w of
+// G reads the 16-byte chunks c with (c / 256) % G == w, four loads in flight
+// per thread, and stores the XOR of every 32-bit word it read into out[w], so
+// that no load can be dropped.
+constexpr int kReadThreads = 256;
+__global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const uint4 *__restrict__ p, int64_t nchunks,
+                                                                uint32_t *__restrict__ out) {
+    __shared__ uint32_t part[kReadThreads / 64];
+    const int64_t stride = (int64_t)gridDim.x * kReadThreads;
+    int64_t c = (int64_t)blockIdx.x * kReadThreads + threadIdx.x;
+    uint32_t v = 0;
+    for (; c + 3 * stride < nchunks; c += 4 * stride) {
+        const uint4 a = p[c], b = p[c + stride], d = p[c + 2 * stride], e = p[c + 3 * stride];
+        v ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ d.x ^ d.y ^ d.z ^ d.w ^ e.x ^ e.y ^ e.z ^ e.w;
+    }
+    for (; c < nchunks; c += stride) {
+        const uint4 a = p[c];
+        v ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    for (int m = 32; m >= 1; m >>= 1) v ^= (uint32_t)__shfl_xor((int)v, m, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
+}
+
 // --------------------------------------------------------------- dequant
 
 // Standalone S3D8 -> channel-INT8 decode (the blog's dequantisation kernel).
@@ -2061,7 +2091,8 @@ bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_
                         const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, void *y,
                         int32_t *acc_out, int cus, hipStream_t stream, bool f3d8, int obf) {
     // (the item's y is only passed on: the kernel stores through it as bf16 when obf)
-    const s3d8_forward_item it{x, M, K, N, tiled, centroids, scales, static_cast<float *>(y), xq, xs, acc_out};
+    const s3d8_forward_item it{x, M, K, N, tiled, tiled_bytes(N, K), centroids, scales, static_cast<float *>(y), xq, xs,
+                               acc_out};
     return launch_gemv_stream_batch(1, &it, cus, stream, f3d8, obf);
 }
 
@@ -2107,12 +2138,16 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
 }
 
 namespace {
-int check_linear_args(const void *tiled, const void *table, const uint16_t *scales, const void *y, int64_t M,
-                      int64_t K, int64_t N) {
+int check_linear_args(const void *tiled, int64_t tiled_size, const void *table, const uint16_t *scales,
+                      const void *y, int64_t M, int64_t K, int64_t N) {
     if (!tiled || !table || !scales || !y) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
     int rc = check_sizes(M, K, N);
     if (rc) return rc;
     if (tiled_bytes(N, K) > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "tiled weights over 2^31 bytes");
+    if (tiled_size < tiled_bytes(N, K))
+        return s3d8::fail(S3D8_ERR_INVALID_ARG,
+                          "tiled_bytes below s3d8_tiled_bytes(N, K): pass the matrix in the tiled layout "
+                          "(s3d8_tile), not the canonical packed bytes");
     if (!aligned16(tiled)) return s3d8::fail(S3D8_ERR_ALIGN, "tiled weights must be 16-byte aligned");
     if (reinterpret_cast<uintptr_t>(table) & 3u)
         return s3d8::fail(S3D8_ERR_ALIGN, "the centroid table must be 4-byte aligned");
@@ -2128,10 +2163,10 @@ int check_variant(int32_t format, int32_t out_type) {
 }
 
 int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int32_t *acc_out,
-                void *stream) {
+                int64_t tiled_size, const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf,
+                int32_t *acc_out, void *stream) {
     if (!xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, tiled_size, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "xq must be 16-byte aligned");
     int cus = 0;
@@ -2178,11 +2213,11 @@ int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
     return launch_status();
 }
 
-int forward_impl(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
-                 bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int8_t *xq, float *xs,
+int forward_impl(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_size,
+                 const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int8_t *xq, float *xs,
                  int32_t *acc_out, void *stream) {
     if (!x || !xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, tiled_size, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(x) || !aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "x and xq must be 16-byte aligned");
     int cus = 0;
@@ -2201,37 +2236,39 @@ int forward_impl(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t 
     }
     rc = s3d8_quant_act(x, M, K, xq, xs, stream);
     if (rc) return rc;
-    return linear_impl(xq, xs, M, K, N, tiled, table, f3d8, scales_bf16, y, obf, acc_out, stream);
+    return linear_impl(xq, xs, M, K, N, tiled, tiled_size, table, f3d8, scales_bf16, y, obf, acc_out, stream);
 }
 }  // namespace
 
 int32_t s3d8_linear(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                    const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16,
-                    float *y, int32_t *acc_out, void *stream) {
-    return linear_impl(xq, xs, M, K, N, tiled, centroids, false, scales_bf16, y, false, acc_out, stream);
+                    const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                    const uint16_t *scales_bf16, float *y, int32_t *acc_out, void *stream) {
+    return linear_impl(xq, xs, M, K, N, tiled, tiled_bytes, centroids, false, scales_bf16, y, false, acc_out,
+                       stream);
 }
 
 int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                       const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
-                       int32_t *acc_out, void *stream) {
+                       int64_t tiled_bytes, const void *table, int32_t format, const uint16_t *scales_bf16, void *y,
+                       int32_t out_type, int32_t *acc_out, void *stream) {
     int rc = check_variant(format, out_type);
     if (rc) return rc;
-    return linear_impl(xq, xs, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+    return linear_impl(xq, xs, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
                        out_type == S3D8_OUT_BF16, acc_out, stream);
 }
 
-int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_bytes,
                      const uint8_t *centroids, const uint16_t *scales_bf16, float *y, int8_t *xq, float *xs,
                      int32_t *acc_out, void *stream) {
-    return forward_impl(x, M, K, N, tiled, centroids, false, scales_bf16, y, false, xq, xs, acc_out, stream);
+    return forward_impl(x, M, K, N, tiled, tiled_bytes, centroids, false, scales_bf16, y, false, xq, xs, acc_out,
+                        stream);
 }
 
-int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, const void *table,
-                        int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type, int8_t *xq, float *xs,
-                        int32_t *acc_out, void *stream) {
+int32_t s3d8_forward_ex(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_bytes,
+                        const void *table, int32_t format, const uint16_t *scales_bf16, void *y, int32_t out_type,
+                        int8_t *xq, float *xs, int32_t *acc_out, void *stream) {
     int rc = check_variant(format, out_type);
     if (rc) return rc;
-    return forward_impl(x, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+    return forward_impl(x, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
                         out_type == S3D8_OUT_BF16, xq, xs, acc_out, stream);
 }
 
@@ -2240,7 +2277,7 @@ int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *
     for (int32_t i = 0; i < count; ++i) {
         const s3d8_forward_item &it = items[i];
         if (!it.x || !it.xq || !it.xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-        int rc = check_linear_args(it.tiled, it.centroids, it.scales_bf16, it.y, it.M, it.K, it.N);
+        int rc = check_linear_args(it.tiled, it.tiled_bytes, it.centroids, it.scales_bf16, it.y, it.M, it.K, it.N);
         if (rc) return rc;
         if (!aligned16(it.x) || !aligned16(it.xq)) return s3d8::fail(S3D8_ERR_ALIGN, "x and xq must be 16-byte aligned");
     }
@@ -2251,8 +2288,8 @@ int32_t s3d8_forward_batch(int32_t count, const s3d8_forward_item *items, void *
     if (launch_gemv_stream_batch(count, items, cus, (hipStream_t)stream)) return launch_status();
     for (int32_t i = 0; i < count; ++i) {
         const s3d8_forward_item &it = items[i];
-        rc = s3d8_forward(it.x, it.M, it.K, it.N, it.tiled, it.centroids, it.scales_bf16, it.y, it.xq, it.xs,
-                          it.acc_out, stream);
+        rc = s3d8_forward(it.x, it.M, it.K, it.N, it.tiled, it.tiled_bytes, it.centroids, it.scales_bf16, it.y,
+                          it.xq, it.xs, it.acc_out, stream);
         if (rc) return rc;
     }
     return S3D8_OK;
@@ -2286,10 +2323,10 @@ int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
 
 namespace {
 int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
-                 const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf, int32_t *acc_out,
-                 int8_t *workspace, int64_t workspace_bytes, void *stream) {
+                 int64_t tiled_size, const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf,
+                 int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
     if (!xq || !xs || !workspace) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
-    int rc = check_linear_args(tiled, table, scales_bf16, y, M, K, N);
+    int rc = check_linear_args(tiled, tiled_size, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
     if (!aligned16(xq) || !aligned16(workspace))
         return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
@@ -2297,7 +2334,8 @@ int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_
     const int64_t T = (N + 2) / 3;
     const int64_t wbytes = s3d8_unfused_workspace_bytes(N, K);
     if (wbytes > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "decoded matrix over 2^31 bytes");
-    if (workspace_bytes < wbytes) return s3d8::fail(S3D8_ERR_INVALID_ARG, "workspace smaller than s3d8_unfused_workspace_bytes");
+    if (workspace_bytes < wbytes)
+        return s3d8::fail(S3D8_ERR_INVALID_ARG, "workspace smaller than s3d8_unfused_workspace_bytes");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
@@ -2355,19 +2393,20 @@ int dequant_impl(const uint8_t *packed, const void *table, bool f3d8, int64_t N,
 }  // namespace
 
 int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                            const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales_bf16, float *y,
-                            int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
-    return unfused_impl(xq, xs, M, K, N, tiled, centroids, false, scales_bf16, y, false, acc_out, workspace,
-                        workspace_bytes, stream);
+                            const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                            const uint16_t *scales_bf16, float *y, int32_t *acc_out, int8_t *workspace,
+                            int64_t workspace_bytes, void *stream) {
+    return unfused_impl(xq, xs, M, K, N, tiled, tiled_bytes, centroids, false, scales_bf16, y, false, acc_out,
+                        workspace, workspace_bytes, stream);
 }
 
 int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
-                               const uint8_t *tiled, const void *table, int32_t format, const uint16_t *scales_bf16,
-                               void *y, int32_t out_type, int32_t *acc_out, int8_t *workspace,
-                               int64_t workspace_bytes, void *stream) {
+                               const uint8_t *tiled, int64_t tiled_bytes, const void *table, int32_t format,
+                               const uint16_t *scales_bf16, void *y, int32_t out_type, int32_t *acc_out,
+                               int8_t *workspace, int64_t workspace_bytes, void *stream) {
     int rc = check_variant(format, out_type);
     if (rc) return rc;
-    return unfused_impl(xq, xs, M, K, N, tiled, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+    return unfused_impl(xq, xs, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
                         out_type == S3D8_OUT_BF16, acc_out, workspace, workspace_bytes, stream);
 }
 
@@ -2392,6 +2431,19 @@ int32_t s3d8_mfma_rate_probe(int32_t iters, int32_t workgroups, int32_t v, int32
     if (rc) return rc;
     hipLaunchKernelGGL(mfma_rate_kernel, dim3((unsigned)workgroups), dim3(kRateThreads), 0, (hipStream_t)stream,
                        (int)iters, (int)v, out);
+    return launch_status();
+}
+
+int32_t s3d8_hbm_read_probe(const void *p, int64_t bytes, int32_t workgroups, uint32_t *out, void *stream) {
+    if (!p || !out) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    if (bytes <= 0 || bytes % 16 != 0) return s3d8::fail(S3D8_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (workgroups < 1 || workgroups > 65536) return s3d8::fail(S3D8_ERR_INVALID_ARG, "1 <= workgroups <= 65536");
+    if (!aligned16(p)) return s3d8::fail(S3D8_ERR_ALIGN, "p must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(out) & 3u) return s3d8::fail(S3D8_ERR_ALIGN, "out must be 4-byte aligned");
+    int rc = check_device(nullptr);
+    if (rc) return rc;
+    hipLaunchKernelGGL(hbm_read_kernel, dim3((unsigned)workgroups), dim3(kReadThreads), 0, (hipStream_t)stream,
+                       static_cast<const uint4 *>(p), bytes / 16, out);
     return launch_status();
 }
 
