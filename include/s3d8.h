@@ -276,6 +276,26 @@ int32_t s3d8_linear_unfused(const int8_t *xq, const float *xs, int64_t M, int64_
                             const uint16_t *scales_bf16, float *y, int32_t *acc_out, int8_t *workspace,
                             int64_t workspace_bytes, void *stream);
 
+/* Size of the device scratch array of s3d8_linear_unfused_noalloc: 64 MiB. */
+#define S3D8_NOALLOC_SCRATCH_BYTES (64LL * 1024 * 1024)
+
+/* s3d8_linear_unfused without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The call allocates nothing: the decoded
+ * matrix goes to a device array of S3D8_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, which that GPU holds from the library's first use on
+ * it until the process ends.  Results are identical to s3d8_linear_unfused.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (e.g. on two streams) race and must be serialised by the caller.
+ *   arguments  as for s3d8_linear_unfused, without the workspace.
+ * Errors: as s3d8_linear_unfused; SHAPE also when the decoded matrix,
+ * s3d8_unfused_workspace_bytes(N, K), is larger than
+ * S3D8_NOALLOC_SCRATCH_BYTES (e.g. the 4096 x 128256 vocabulary projection,
+ * 525 MB decoded). */
+int32_t s3d8_linear_unfused_noalloc(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                                    const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                                    const uint16_t *scales_bf16, float *y, int32_t *acc_out, void *stream);
+
 /* Decode a whole matrix to channel-INT8 ([PAPER] Eq. 1 without alpha; the
  * blog's standalone S3D8 -> INT8 dequantisation).
  *   packed     device uint8 [ceil(N/3)][K], 16-B aligned.

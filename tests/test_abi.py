@@ -181,6 +181,28 @@ def test_hbm_read_probe_validation():
     assert L.s3d8_hbm_read_probe(A16, 16, 1, A16 + 2, None) == _lib.S3D8_ERR_ALIGN
 
 
+def test_noalloc_validation():
+    """s3d8_linear_unfused_noalloc refuses, before any GPU work, a matrix
+    whose decoded size exceeds its 64 MiB device scratch, and validates the
+    rest like s3d8_linear_unfused."""
+    L = _lib.lib()
+    assert _lib.S3D8_NOALLOC_SCRATCH_BYTES == 64 * 2 ** 20
+    with open(os.path.join(ROOT, "include", "s3d8.h")) as f:
+        assert "#define S3D8_NOALLOC_SCRATCH_BYTES (64LL * 1024 * 1024)" in f.read()
+    K, N = 4096, 128256
+    assert L.s3d8_unfused_workspace_bytes(N, K) > _lib.S3D8_NOALLOC_SCRATCH_BYTES
+    rc = L.s3d8_linear_unfused_noalloc(A16, A16, 17, K, N, A16, TB, A16, A16, A16, None, None)
+    assert rc == _lib.S3D8_ERR_SHAPE and "scratch" in L.s3d8_last_error().decode()
+    assert L.s3d8_linear_unfused_noalloc(A16, A16, 1, 24, 9, A16, TB, A16, A16, A16, None, None) \
+        == _lib.S3D8_ERR_SHAPE
+    assert L.s3d8_linear_unfused_noalloc(A_ODD, A16, 1, 64, 9, A16, TB, A16, A16, A16, None, None) \
+        == _lib.S3D8_ERR_ALIGN
+    assert L.s3d8_linear_unfused_noalloc(A16, A16, 1, 4096, 14336, A16, 1000, A16, A16, A16, None, None) \
+        == _lib.S3D8_ERR_INVALID_ARG
+    assert L.s3d8_linear_unfused_noalloc(A16, A16, 0, 64, 9, A16, TB, A16, A16, A16, None, None) \
+        == _lib.S3D8_ERR_INVALID_ARG
+
+
 def test_mfma_rate_probe_validation():
     L = _lib.lib()
     assert L.s3d8_mfma_rate_probe(1, 1, 1, None, None) == _lib.S3D8_ERR_INVALID_ARG

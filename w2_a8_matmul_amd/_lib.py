@@ -17,6 +17,7 @@ S3D8_ERR_ALIGN = 3
 S3D8_ERR_HIP = 4
 S3D8_ERR_NOMEM = 5
 S3D8_ERR_DEVICE = 6
+S3D8_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -48,6 +49,7 @@ SIGNATURES = {
     "s3d8_dequant_ex": (_I32, [_P, _P, _I32, _I64, _I64, _P, _P]),
     "s3d8_mfma_rate_probe": (_I32, [_I32, _I32, _I32, _P, _P]),
     "s3d8_hbm_read_probe": (_I32, [_P, _I64, _I32, _P, _P]),
+    "s3d8_linear_unfused_noalloc": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P]),
 }
 
 

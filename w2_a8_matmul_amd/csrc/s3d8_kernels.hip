@@ -25,6 +25,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "s3d8.h"
 #include "s3d8_internal.h"
@@ -2321,24 +2322,74 @@ int64_t s3d8_unfused_workspace_bytes(int64_t N, int64_t K) {
     return (3 * ((N + 2) / 3) + 31) / 32 * ((K + 63) / 64) * 2048;
 }
 
+// ------------------------------------------------- no-allocation unfused path
+
+// Device-side workspace of s3d8_linear_unfused_noalloc: the decoded INT8
+// matrix lives in this file-scope array instead of a caller's buffer, for
+// callers that cannot allocate device memory.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` is only a
+// stand-in for the symbol, never a device address: the address is looked up
+// once per device with hipGetSymbolAddress (noalloc_scratch) and only that
+// pointer is handed to kernels.  Every call on one GPU shares its copy, so
+// calls that overlap on one GPU (different streams) race.  What a previous
+// call left there needs no clearing: the decode overwrites every byte of the
+// matrix, and the bytes it leaves alone (channels past the last triple,
+// columns past K in the last 64-column block) only meet zero activations or
+// feed outputs that are never stored.
+constexpr int64_t kNoAllocScratchBytes = S3D8_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes == int64_t(64) << 20, "the header states 64 MiB");
+static __device__ __align__(256) int8_t scratch[kNoAllocScratchBytes];
+
 namespace {
+constexpr int kMaxDevices = 64;
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (after check_device has accepted the device).
+int noalloc_scratch(int8_t **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return s3d8::fail(S3D8_ERR_HIP, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return s3d8::fail(S3D8_ERR_DEVICE, "device ordinal out of range");
+    static std::mutex mu;
+    static int8_t *ptr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return s3d8::fail(S3D8_ERR_HIP, "hipGetSymbolAddress of the scratch array failed");
+        ptr[dev] = static_cast<int8_t *>(p);
+    }
+    *out = ptr[dev];
+    return S3D8_OK;
+}
+
+// noalloc: the workspace is the library's scratch array (workspace and
+// workspace_bytes are ignored), looked up once the arguments are validated.
 int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
                  int64_t tiled_size, const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf,
-                 int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream) {
-    if (!xq || !xs || !workspace) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+                 int32_t *acc_out, int8_t *workspace, int64_t workspace_bytes, void *stream, bool noalloc = false) {
+    if (!xq || !xs || (!noalloc && !workspace)) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
     int rc = check_linear_args(tiled, tiled_size, table, scales_bf16, y, M, K, N);
     if (rc) return rc;
-    if (!aligned16(xq) || !aligned16(workspace))
+    if (!aligned16(xq) || (!noalloc && !aligned16(workspace)))
         return s3d8::fail(S3D8_ERR_ALIGN, "xq and workspace must be 16-byte aligned");
     if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported");
     const int64_t T = (N + 2) / 3;
     const int64_t wbytes = s3d8_unfused_workspace_bytes(N, K);
     if (wbytes > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "decoded matrix over 2^31 bytes");
-    if (workspace_bytes < wbytes)
+    if (noalloc && wbytes > kNoAllocScratchBytes)
+        return s3d8::fail(S3D8_ERR_SHAPE,
+                          "the decoded matrix exceeds the 64 MiB device scratch of s3d8_linear_unfused_noalloc "
+                          "(s3d8_unfused_workspace_bytes(N, K) > S3D8_NOALLOC_SCRATCH_BYTES); use "
+                          "s3d8_linear_unfused with a workspace");
+    if (!noalloc && workspace_bytes < wbytes)
         return s3d8::fail(S3D8_ERR_INVALID_ARG, "workspace smaller than s3d8_unfused_workspace_bytes");
     int cus = 0;
     rc = check_device(&cus);
     if (rc) return rc;
+    if (noalloc) {
+        rc = noalloc_scratch(&workspace);
+        if (rc) return rc;
+    }
     const int KB = (int)((K + 63) / 64);
     const int64_t nchunks = tiled_bytes(N, K) / 16;
     int64_t blocks = (nchunks + kDequantThreads - 1) / kDequantThreads;
@@ -2408,6 +2459,13 @@ int32_t s3d8_linear_unfused_ex(const int8_t *xq, const float *xs, int64_t M, int
     if (rc) return rc;
     return unfused_impl(xq, xs, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
                         out_type == S3D8_OUT_BF16, acc_out, workspace, workspace_bytes, stream);
+}
+
+int32_t s3d8_linear_unfused_noalloc(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                                    const uint8_t *tiled, int64_t tiled_bytes, const uint8_t *centroids,
+                                    const uint16_t *scales_bf16, float *y, int32_t *acc_out, void *stream) {
+    return unfused_impl(xq, xs, M, K, N, tiled, tiled_bytes, centroids, false, scales_bf16, y, false, acc_out,
+                        nullptr, 0, stream, true);
 }
 
 int32_t s3d8_dequant(const uint8_t *packed, const uint8_t *centroids, int64_t N, int64_t K, int8_t *w,
