@@ -45,6 +45,38 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA, 5.0 POPS
 MALL_BYTES = 256 * 2 ** 20   # Infinity Cache
 METRIC = "effective weight GB/s (% HBM peak) at M=1; INT8 TOPS (% MFMA peak) at M=2048"
+SETTLE_S = 0.2     # sustained load before the headline region (clock settle)
+NSAMPLES = 200     # per-call samples behind the median and its interval
+SAMPLE_REPS = 5    # replays of the R-step sequence per sample
+
+# The pages' own throughput figures for this layer, all on Arm CPUs, quoted as
+# context (GMAC/s of the fused S3D8 kernel at m = 1, of the S3D8 -> INT8 path
+# at m = 128; the paper's Table 2 and Appendix table, the blog's "Fast? How
+# fast?" section).  Not a target: other hardware, other precision of timing.
+PAGES_CONTEXT = [
+    {"shape_mkn": [1, 4096, 14336], "hardware": "Google Pixel 8a, 5 cores", "s3d8_GMACs": 33.8,
+     "int8_GMACs": 26.5, "bf16_GMACs": 13.6, "source": "paper Table 2 (text.mlp.up); blog 'Fast? How fast?'"},
+    {"shape_mkn": [1, 4096, 14336], "hardware": "AWS Graviton4, 96 Neoverse V2 cores", "s3d8_GMACs": 1031,
+     "int8_GMACs": 461, "bf16_GMACs": 236, "source": "paper Appendix table (Graviton4)"},
+    {"shape_mkn": [128, 4096, 14336], "hardware": "Google Pixel 8a, 5 cores", "s3d8_GMACs": 197.7,
+     "int8_GMACs": 201.1, "bf16_GMACs": 76.3, "source": "paper Table 2 (text.mlp.up, m = 128)"},
+    {"shape_mkn": [128, 4096, 14336], "hardware": "AWS Graviton4, 96 Neoverse V2 cores", "s3d8_GMACs": 6994,
+     "int8_GMACs": 7700, "bf16_GMACs": 3492, "source": "paper Appendix table (Graviton4)"},
+    {"shape_mkn": [1601, 1280, 5120], "hardware": "Google Pixel 8a, 5 cores", "s3d8_GMACs": 211.8,
+     "int8_GMACs": 206.1, "bf16_GMACs": 116.5, "source": "paper Table 2 (vision.mlp.up)"},
+]
+
+
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), for the CPU baseline."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def log(msg):
@@ -106,6 +138,7 @@ def graph_launch_us(torch, fns, reps, warm_s=0.1):
             break
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
+    g.replay()  # untimed: keeps the GPU busy while the timed replays are submitted
     a.record()
     for _ in range(reps):
         g.replay()
@@ -117,10 +150,9 @@ def graph_launch_us(torch, fns, reps, warm_s=0.1):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # default warm-up: about 0.2 s of steps, long enough for the clocks to
-    # settle under sustained load (the timed steps then run at steady state)
+    # (the warm-up steps are followed by a time-based settle, SETTLE_S)
     ap.add_argument("--steps", type=int, default=5600)
-    ap.add_argument("--warmup", type=int, default=22400)
+    ap.add_argument("--warmup", type=int, default=280)
     ap.add_argument("--pack-iters", type=int, default=25)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -188,32 +220,60 @@ def main():
                 step(r)
     torch.cuda.synchronize()
 
-    for i in range(0, args.warmup, R):
+    # warm-up: the W steps asked for (whole replays of the R-step graph),
+    # then replays until SETTLE_S seconds of sustained load have passed,
+    # whatever W is: the clocks take a few tens of milliseconds to settle
+    for i in range(max(1, -(-args.warmup // R))):
         graph.replay()
     torch.cuda.synchronize()
+    t_settle = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_settle:
+        graph.replay()
+        torch.cuda.synchronize()
     log(f"timing {args.steps} steps (graph of {R} steps, R={R} weight copies)")
-    # an event after every replay as well: each replay of R launches is one
-    # sample of the per-call time (median and bootstrap interval below);
-    # `value` is the whole timed region
-    nrep = args.steps // R
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(nrep + 1)]
+    # the timed region: exactly `steps` launches between two events on the
+    # launching stream.  One untimed replay is queued in front of the start
+    # event, after the synchronisation, so that the GPU is still busy with it
+    # while the host submits the timed launches: the region then holds the
+    # steps' GPU time and not the host's graph-launch latency (about 5 us per
+    # replay, which a region of only a few steps would otherwise carry).
+    start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    marks[0].record()
-    for i in range(nrep):
+    graph.replay()
+    start.record()
+    for i in range(args.steps // R):
         graph.replay()
-        marks[i + 1].record()
     if graph_rem is not None:
         graph_rem.replay()
     end.record()
     torch.cuda.synchronize()
-    ms_total = marks[0].elapsed_time(end)
+    ms_total = start.elapsed_time(end)
     ms_per_step = ms_total / args.steps
     value = weight_bytes / (ms_per_step * 1e-3) / 1e9
-    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) * 1e3 / R for i in range(nrep)])
-    timing = {"samples": int(nrep), "launches_per_sample": R,
+    # per-call samples for the median and its 95 % bootstrap interval (the
+    # pages' own statistic): NSAMPLES replays of a graph of SAMPLE_REPS * R
+    # launches, an event after each, whatever `steps` is
+    gs = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gs):
+        for _ in range(SAMPLE_REPS):
+            for r in range(R):
+                step(r)
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(NSAMPLES + 1)]
+    gs.replay()
+    marks[0].record()
+    for i in range(NSAMPLES):
+        gs.replay()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    per_call = np.array([marks[i].elapsed_time(marks[i + 1]) * 1e3 / (SAMPLE_REPS * R) for i in range(NSAMPLES)])
+    ci = bootstrap_ci(per_call)
+    timing = {"samples": NSAMPLES, "launches_per_sample": SAMPLE_REPS * R, "settle_s": SETTLE_S,
               "per_call_us_median": round(float(np.median(per_call)), 3),
-              "per_call_us_ci95": [round(v, 3) for v in bootstrap_ci(per_call)]}
+              "per_call_us_ci95": [round(v, 3) for v in ci],
+              "per_call_us_min_max": [round(float(per_call.min()), 3), round(float(per_call.max()), 3)],
+              "timed_region_us_per_step": round(ms_per_step * 1e3, 3)}
 
     # dominant kernel: the fused quantise + decode GEMV launched by
     # s3d8_forward.  At M=1 a step is exactly one launch of it, so its
@@ -280,17 +340,38 @@ def main():
     cs_us = graph_launch_us(torch, [lambda r=r: same[2 * r + 1].copy_(same[2 * r]) for r in range(R)], 10)
     del same
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    # read-only streams: the c1 matrix's size (rounded down to 16 bytes)
+    # through R distinct buffers, and 1 GiB; the probe at 1 to 8 workgroups
+    # per CU, the best kept
+    rsize = weight_bytes // 16 * 16
+    rbufs = [torch.empty((rsize,), dtype=torch.uint8, device=dev) for _ in range(R)]
+    rout = torch.empty((8 * cus,), dtype=torch.int32, device=dev)
+    rd_us = {}
+    for wpc in (1, 2, 4, 8):
+        rd_us[wpc] = graph_launch_us(torch, [lambda r=r, wpc=wpc: s3d8.hbm_read_probe(rbufs[r], wpc * cus, out=rout)
+                                             for r in range(R)], 10)
+    del rbufs
+    rd_best = min(rd_us, key=rd_us.get)
+    rbig = torch.empty((2 ** 30,), dtype=torch.uint8, device=dev)
+    rbig_us = graph_launch_us(torch, [lambda: s3d8.hbm_read_probe(rbig, rd_best * cus, out=rout)], 5)
+    del rbig
     pr_out, pr_ops = s3d8.mfma_rate_probe(2000, 4 * cus, 1, device=dev)
     pr_us = graph_launch_us(torch, [lambda: s3d8.mfma_rate_probe(2000, 4 * cus, 1, out=pr_out)], 5)
     ceilings = {"hbm_copy_1GiB_GBs": round(2 * 2 ** 30 / (cp_us * 1e-6) / 1e9, 1),
                 "hbm_copy_c1_size_GBs": round(2 * weight_bytes / (cs_us * 1e-6) / 1e9, 1),
                 "hbm_copy_c1_size_us": round(cs_us, 3),
+                "hbm_read_c1_size_us": round(rd_us[rd_best], 3),
+                "hbm_read_c1_size_GBs": round(rsize / (rd_us[rd_best] * 1e-6) / 1e9, 1),
+                "hbm_read_c1_size_us_by_workgroups_per_cu": {str(k): round(v, 3) for k, v in rd_us.items()},
+                "hbm_read_1GiB_GBs": round(2 ** 30 / (rbig_us * 1e-6) / 1e9, 1),
+                "hbm_read_probe": f"s3d8_hbm_read_probe, {rsize} bytes through {R} buffers, 16-byte loads",
                 "int8_mfma_probe_TOPS": round(pr_ops / (pr_us * 1e-6) / 1e12, 1),
                 "int8_mfma_probe": f"{4 * cus} workgroups x 4 waves, 2000 rounds of 4 independent "
                                    f"v_mfma_i32_32x32x32_i8 each"}
     log(f"ceilings: copy 1 GiB {ceilings['hbm_copy_1GiB_GBs']} GB/s, copy {weight_bytes} B "
-        f"{cs_us:.2f} us ({ceilings['hbm_copy_c1_size_GBs']} GB/s), INT8 MFMA probe "
-        f"{ceilings['int8_mfma_probe_TOPS']} TOPS")
+        f"{cs_us:.2f} us ({ceilings['hbm_copy_c1_size_GBs']} GB/s), read {rsize} B {rd_us[rd_best]:.2f} us "
+        f"({ceilings['hbm_read_c1_size_GBs']} GB/s), read 1 GiB {ceilings['hbm_read_1GiB_GBs']} GB/s, "
+        f"INT8 MFMA probe {ceilings['int8_mfma_probe_TOPS']} TOPS")
 
     # ---------------------------------------------------------------- one decoder-layer step (c2)
     # the seven linears of a decoder layer at one token, each with its own
@@ -436,6 +517,23 @@ def main():
         ops = 2.0 * lp.M * lp.K * lp.N
         tops = ops / (g_mean_us * 1e-6) / 1e12
         log(f"prefill GEMM {lp.name}: fused {g_mean_us:.1f} us -> {tops:.1f} TOPS")
+        # context: the vendor library's plain INT8 GEMM (torch._int_mm, which
+        # runs hipBLASLt on ROCm) on the same shape with INT8 weights: no
+        # decode, INT32 output, i.e. what an INT8-weight model would run
+        lib_gemm = None
+        try:
+            wi8 = [torch.randint(-127, 128, (lp.N, lp.K), dtype=torch.int8, device=dev) for _ in range(Rp)]
+            torch._int_mm(xqp, wi8[0].t())
+            torch.cuda.synchronize()
+            l_us = graph_launch_us(torch, [lambda r=r: torch._int_mm(xqp, wi8[r].t()) for r in range(Rp)], 20)
+            lib_gemm = {"call": "torch._int_mm(xq [M][K] int8, w[N][K].t() int8) -> int32 [M][N]",
+                        "us": round(l_us, 2), "TOPS": round(ops / (l_us * 1e-6) / 1e12, 1),
+                        "frac": round(ops / (l_us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
+            log(f"library INT8 GEMM (torch._int_mm) {l_us:.1f} us -> {lib_gemm['TOPS']} TOPS")
+            del wi8
+        except Exception as e:  # not every torch build routes _int_mm to a GPU library
+            lib_gemm = {"error": f"{type(e).__name__}: {e}"[:200]}
+            log(f"library INT8 GEMM unavailable: {lib_gemm['error']}")
         # the pages' strategy for many rows: decode once to INT8, then an
         # INT8 GEMM (two launches per call)
         ws = torch.empty((s3d8.unfused_workspace_bytes(lp.N, lp.K),), dtype=torch.int8, device=dev)
@@ -468,6 +566,7 @@ def main():
                          "frac_of_probe": round(tops / ceilings["int8_mfma_probe_TOPS"], 4),
                          "traffic": measured_traffic("gemm_c3", None),
                          "kernel": "gemm_kernel (fused decode + INT8 MFMA, via s3d8_linear)"},
+            "library_int8_gemm": lib_gemm,
             "unfused": {"value": round(u_tops, 2), "unit": "INT8 TOPS", "us_per_call": round(u_mean_us, 2),
                         "frac": round(u_tops / INT8_PEAK_TOPS, 4),
                         "kernels": "dequant_tiled_kernel + gemm_i8_kernel (s3d8_linear_unfused)"},
@@ -522,7 +621,7 @@ def main():
                 break
         el = time.perf_counter() - t0
         cpu = {"value": round(weight_bytes * n / el / 1e9, 4), "unit": "GB/s", "cores": threads,
-               "kind": "oracle",
+               "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "kind": "oracle",
                "sample": f"full {lin.name} step (quantise, decode every weight, naive int dot "
                          f"products, fp32 epilogue) repeated {n} times in {el:.1f} s"}
         log(f"cpu oracle: {cpu['value']} GB/s on {threads} threads")
@@ -546,10 +645,19 @@ def main():
                    "weight_copies": R, "graph_steps": R},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "gemv_stream_kernel (fused quantise + decode GEMV, via s3d8_forward)", "kernel_us": round(lin_mean_us, 3),
-                     "algorithmic_bytes": kernel_bytes,
-                     "frac_of_copy_1GiB": round(achieved / ceilings["hbm_copy_1GiB_GBs"], 4)},
+                     "kernel": "gemv_stream_kernel (fused quantise + decode GEMV, via s3d8_forward)",
+                     "kernel_us": round(lin_mean_us, 3), "algorithmic_bytes": kernel_bytes,
+                     "frac_of_copy_1GiB": round(achieved / ceilings["hbm_copy_1GiB_GBs"], 4),
+                     "frac_of_same_size_read": round(ceilings["hbm_read_c1_size_us"] / lin_mean_us, 4)},
         "timing": timing,
+        "context_pages_arm": {"note": "the pages' own figures (Arm CPUs), quoted with their hardware; "
+                                      "context, not a target",
+                              "figures": PAGES_CONTEXT,
+                              "this_run_GMACs": {"[1, 4096, 14336] fused S3D8, s3d8_forward":
+                                                 round(K * N / (ms_per_step * 1e-3) / 1e9, 1),
+                                                 "[2048, 4096, 14336] fused S3D8, s3d8_linear":
+                                                 None if prefill is None else
+                                                 round(prefill["value"] * 1e3 / 2, 1)}},
         "ceilings": ceilings,
         "quant_act_us": round(qa_mean_us, 3),
         "prefill": prefill,
@@ -560,7 +668,7 @@ def main():
         "variants": variants,
         "cpu_baseline": cpu,
     }
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out, allow_nan=False), flush=True)
 
 
 if __name__ == "__main__":
