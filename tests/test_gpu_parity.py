@@ -529,3 +529,42 @@ def test_linear_unfused_workspace_reuse(gpu):
         _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
         np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
         check_y(y.cpu().numpy(), y_r)
+
+
+# ------------------------------------------------------------------ tiles per workgroup
+# One token row with between one and two tiles of 16 triples per CU (256 CUs
+# on MI355X), where some workgroups of the streaming GEMV take a second tile:
+# 257, 299, 512 and 513 tiles, K from 1040 to 14336 (one to four float4 of
+# activations per lane).  Every output, the codes and the scales against the
+# oracle, in both formats and output types.
+ONE_TILE = [(4096, 14336), (8192, 14336), (5120, 12336), (4096, 24576), (4096, 24624), (1040, 12400),
+            (14336, 12336)]
+
+
+@pytest.mark.parametrize("K,N", ONE_TILE)
+def test_forward_tiles_per_workgroup(gpu, K, N):
+    C, alpha, packed = random_format([2140, K, N], N, K)
+    x = workloads.gaussian_matrix([2141, K, N], 1, K)
+    xq, xs, acc, y = run_forward(x, C, alpha, packed, N, gpu)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    np.testing.assert_array_equal(xq, xq_r)
+    np.testing.assert_array_equal(xs, xs_r)
+    np.testing.assert_array_equal(acc, acc_r)
+    check_y(y, y_r)
+
+
+@pytest.mark.parametrize("K,N", [(4096, 14336), (8192, 12336)])
+def test_forward_tiles_per_workgroup_3d8_bf16(gpu, K, N):
+    _, alpha, packed = random_format([2150, K, N], N, K)
+    T3 = workloads.signed_table([2151, K])
+    x = workloads.gaussian_matrix([2152, K], 1, K)
+    tiled = s3d8.tile(dev(packed, gpu), N)
+    y, xq, xs, acc = s3d8.forward(dev(x, gpu), tiled, dev(T3, gpu), dev(alpha.view(np.int16), gpu), N,
+                                  return_all=True, fmt="3d8", out="bf16")
+    torch.cuda.synchronize()
+    xq_r, xs_r = oracle.quant_act(x)
+    acc_r = oracle.linear_acc_3d8(xq_r, packed, T3, N)
+    y_r = oracle.epilogue(acc_r, xs_r, alpha, N)
+    np.testing.assert_array_equal(xq.cpu().numpy(), xq_r)
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+    np.testing.assert_array_equal(y.view(torch.int16).cpu().numpy().view(np.uint16), oracle.to_bf16(y_r))

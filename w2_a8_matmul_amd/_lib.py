@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs3d8.so")
+# S3D8_LIB selects another build of the library (e.g. the sanitizer build of
+# the host code, build.py --sanitize); by default the in-tree libs3d8.so
+LIB_PATH = os.environ.get("S3D8_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libs3d8.so")
 
 S3D8_OK = 0
 S3D8_ERR_INVALID_ARG = 1
