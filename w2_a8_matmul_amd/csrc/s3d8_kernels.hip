@@ -131,22 +131,64 @@ __device__ __forceinline__ v4i rsrc_words(const void *p, uint32_t bytes) {
     return v4i{(int32_t)(uint32_t)a, (int32_t)((uint32_t)(a >> 32) & 0xFFFFu), (int32_t)bytes, kRsrcWord3};
 }
 
-// 16 bytes per lane from buffer offset voff into LDS at lds + 16 * lane
-// (buffer_load_dwordx4 with the LDS bit; M0 holds the LDS base and is
-// restored afterwards).  An offset past the buffer writes zeros.  The load
-// counts in vmcnt like any vector load; the compiler does not see it, so the
-// caller waits for it explicitly.
-__device__ __forceinline__ void load_to_lds16(uint32_t lds, uint32_t voff, v4i rsrc) {
+// 16 bytes per lane from buffer offset voff + soff into LDS at lds + 16 *
+// lane (buffer_load_dwordx4 with the LDS bit; M0 holds the LDS base and is
+// restored afterwards).  soff, the instruction's scalar offset, lets per-lane
+// offsets stay loop-invariant.  A lane whose voff is at or past the buffer
+// size (kOOB) writes zeros; callers keep soff below 2^31 so that voff + soff
+// never wraps, and keep voff + soff inside the buffer for every other lane.
+// The load counts in vmcnt like any vector load; the compiler does not see
+// it, so the caller waits for it explicitly.
+__device__ __forceinline__ void load_to_lds16_so(uint32_t lds, uint32_t voff, uint32_t soff, v4i rsrc) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
         "s_nop 0\n\t"
-        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "s"(lds), "v"(voff), "s"(rsrc)
+        : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
         : "memory");
+}
+
+// The LDS-DMA loads of one GEMM block in one go: activation loads a0..a(NA-1)
+// from buffer ra with scalar offset sa, then weight loads w0, w1 from buffer
+// rw with scalar offset sw (the block's byte offset rides in the loads' soffset
+// field, so the per-lane offsets stay loop-invariant), each into LDS at its
+// own base (through M0, saved once around the batch).  Offsets and waits as
+// for load_to_lds16_so.
+template <int NA>
+__device__ __forceinline__ void load_block_to_lds(const uint32_t (&lds)[NA + 2], const uint32_t (&voff)[NA + 2],
+                                                  v4i ra, uint32_t sa, v4i rw, uint32_t sw) {
+    uint32_t saved;
+    static_assert(NA == 2 || NA == 3, "two or three activation loads per block");
+    if constexpr (NA == 3) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %11, %12 offen lds\n\t"
+            "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %11, %12 offen lds\n\t"
+            "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %11, %12 offen lds\n\t"
+            "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %9, %13, %14 offen lds\n\t"
+            "s_mov_b32 m0, %5\n\ts_nop 0\n\tbuffer_load_dwordx4 %10, %13, %14 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(lds[0]), "s"(lds[1]), "s"(lds[2]), "s"(lds[3]), "s"(lds[4]), "v"(voff[0]), "v"(voff[1]),
+              "v"(voff[2]), "v"(voff[3]), "v"(voff[4]), "s"(ra), "s"(sa), "s"(rw), "s"(sw)
+            : "memory");
+    } else {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %10 offen lds\n\t"
+            "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %10 offen lds\n\t"
+            "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %7, %11, %12 offen lds\n\t"
+            "s_mov_b32 m0, %4\n\ts_nop 0\n\tbuffer_load_dwordx4 %8, %11, %12 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(lds[0]), "s"(lds[1]), "s"(lds[2]), "s"(lds[3]), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]),
+              "v"(voff[3]), "s"(ra), "s"(sa), "s"(rw), "s"(sw)
+            : "memory");
+    }
 }
 
 // Stage the weight table into LDS (clw: kTableWords3D8 words), then build the
@@ -1338,18 +1380,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 
     const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), wbase = S3D8_LDS_OFFSET(&wbuf[0][0]);
     const uint32_t sbase = S3D8_LDS_OFFSET(&spill[0]);
-    // ND loads per wave and block, also for blocks past the end (they read
-    // nothing), so that every wait below counts the same
+    // In the last block the activation chunks at or past K must read zeros
+    // (the weights there decode to +-C[0], not to zero): atail holds the
+    // per-lane offsets of that block.
+    const int ktail = K - 64 * (KB - 1);
+    uint32_t atail[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) atail[j] = acol[j] < ktail ? aoff[j] : kOOB;
+    // ND loads per wave and block, also for the blocks past the end, so that
+    // every wait below counts the same: those re-read the last block into a
+    // slot that is never read.  The per-lane offsets are block 0's; the
+    // block's byte offset goes in the scalar offset of the loads.
     auto issue = [&](int kb, int slot) {
-        const bool live = kb < KB;
+        const int kbc = kb < KB ? kb : KB - 1;
+        const bool tail = kb >= KB - 1;
+        uint32_t lds[ND], vo[ND];
 #pragma unroll
-        for (int j = 0; j < NA; ++j)
-            load_to_lds16(NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j) : sbase,
-                          (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
+        for (int j = 0; j < NA; ++j) {
+            lds[j] = NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j) : sbase;
+            vo[j] = tail ? atail[j] : aoff[j];
+        }
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-            load_to_lds16(wbase + (uint32_t)(kGemmBF * 1024) * slot + 2048u * wave + 1024u * kh,
-                          (live && woff[kh] != kOOB) ? woff[kh] + 1024u * kb : kOOB, rw);
+        for (int kh = 0; kh < 2; ++kh) {
+            lds[NA + kh] = wbase + (uint32_t)(kGemmBF * 1024) * slot + 2048u * wave + 1024u * kh;
+            vo[NA + kh] = woff[kh];
+        }
+        load_block_to_lds<NA>(lds, vo, rx, 64u * (uint32_t)kbc, rw, 1024u * (uint32_t)kbc);
     };
 
     // A operand of row tile i, k-half kh: row 32 i + c32, chunk 2 kh + h
@@ -1720,22 +1776,30 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     }
     const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0]), bbase = S3D8_LDS_OFFSET(&bbuf[0][0]);
     const uint32_t sbase = abase + (uint32_t)(kSlots * BM * 64);
-    // ND loads per wave and block, also past the end (they read nothing), so
-    // that every wait below counts the same
+    // activation chunks at or past K in the last block read zeros (the
+    // workspace bytes there are not written by the decode)
+    const int ktail = K - 64 * (KB - 1);
+    uint32_t atail[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) atail[j] = acol[j] < ktail ? aoff[j] : kOOB;
+    // ND loads per wave and block, also for the blocks past the end, so that
+    // every wait below counts the same: those re-read the last block into a
+    // slot that is never read.  The block's byte offset goes in the scalar
+    // offset of the loads; the per-lane offsets are block 0's.
     auto issue = [&](int kb, int slot) {
-        const bool live = kb < KB;
+        const int kbc = kb < KB ? kb : KB - 1;
+        const bool tail = kb >= KB - 1;
 #pragma unroll
         for (int j = 0; j < NA; ++j)
-            load_to_lds16(NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j) : sbase,
-                          (live && aoff[j] != kOOB && kb * 64 + acol[j] < K) ? aoff[j] + 64u * kb : kOOB, rx);
+            load_to_lds16_so(NA * wave + j < 2 * RT ? abase + (uint32_t)(BM * 64) * slot + 1024u * (NA * wave + j)
+                                                    : sbase,
+                             tail ? atail[j] : aoff[j], 64u * (uint32_t)kbc, rx);
 #pragma unroll
         for (int ct = 0; ct < 3; ++ct)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const bool ok = live && boff[ct] != kOOB;
-                load_to_lds16(bbase + (uint32_t)(4 * 6 * 1024) * slot + 6144u * wave + 1024u * (2 * ct + kh),
-                              ok ? boff[ct] + 2048u * kb + 1024u * kh : kOOB, rw);
-            }
+            for (int kh = 0; kh < 2; ++kh)
+                load_to_lds16_so(bbase + (uint32_t)(4 * 6 * 1024) * slot + 6144u * wave + 1024u * (2 * ct + kh),
+                                 boff[ct] + 1024u * kh, 2048u * (uint32_t)kbc, rw);
     };
 
     const int swz = (c32 >> 2) & 3;
