@@ -91,7 +91,7 @@ def _edge_rows(K):
 
 
 @pytest.mark.parametrize("M,K", [(1, 16), (1, 256), (3, 48), (8, 4096), (1, 14336), (37, 1280),
-                                 (1601, 5120), (2048, 4096)])
+                                 (1601, 5120), (2048, 4096), (6, 16384), (7, 16400), (2, 20000)])
 def test_quant_act_matches_oracle(gpu, M, K):
     x = workloads.gaussian_matrix([2001, M, K], M, K)
     if M >= 6:

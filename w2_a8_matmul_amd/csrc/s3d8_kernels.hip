@@ -224,9 +224,12 @@ __device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *c
 
 // One workgroup per token row: absmax reduction, then s = a / 127 and
 // xq = clamp(rne(x / s), -127, 127) with IEEE fp32 division (the paper's
-// channel-scaled INT8 activations, one scale per token).
+// channel-scaled INT8 activations, one scale per token).  NV > 0: the row is
+// read once, NV float4 per thread held in registers between the reduction
+// and the quantisation (K <= 1024 NV); NV = 0: any K, the row is read twice.
 constexpr int kQuantThreads = 256;
 
+template <int NV>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *__restrict__ x, int K,
                                                                   int8_t *__restrict__ xq,
                                                                   float *__restrict__ xs) {
@@ -234,10 +237,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *_
     const int64_t row = blockIdx.x;
     const float4 *xr = reinterpret_cast<const float4 *>(x + row * K);
     const int n4 = K >> 2;
+    float4 v[NV > 0 ? NV : 1];
     float a = 0.0f;
-    for (int i = threadIdx.x; i < n4; i += kQuantThreads) {
-        const float4 v = xr[i];
-        a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    auto amax4 = [](float4 q) { return fmaxf(fmaxf(fabsf(q.x), fabsf(q.y)), fmaxf(fabsf(q.z), fabsf(q.w))); };
+    if constexpr (NV > 0) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = threadIdx.x + j * kQuantThreads;
+            v[j] = i < n4 ? xr[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+#pragma unroll
+        for (int j = 0; j < NV; ++j) a = fmaxf(a, amax4(v[j]));
+    } else {
+        for (int i = threadIdx.x; i < n4; i += kQuantThreads) a = fmaxf(a, amax4(xr[i]));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off, 64));
@@ -249,19 +261,38 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *_
     const float s = a / 127.0f;
     if (threadIdx.x == 0) xs[row] = (a == 0.0f) ? 0.0f : s;
     char4 *qr = reinterpret_cast<char4 *>(xq + row * K);
-    for (int i = threadIdx.x; i < n4; i += kQuantThreads) {
-        const float4 v = xr[i];
+    auto quant4 = [&](float4 q) {
+        if (a == 0.0f) return make_char4(0, 0, 0, 0);
         char4 o;
-        if (a == 0.0f) {
-            o = make_char4(0, 0, 0, 0);
-        } else {
-            o.x = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(v.x / s)));
-            o.y = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(v.y / s)));
-            o.z = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(v.z / s)));
-            o.w = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(v.w / s)));
+        o.x = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(q.x / s)));
+        o.y = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(q.y / s)));
+        o.z = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(q.z / s)));
+        o.w = (signed char)fminf(127.0f, fmaxf(-127.0f, rintf(q.w / s)));
+        return o;
+    };
+    if constexpr (NV > 0) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int i = threadIdx.x + j * kQuantThreads;
+            if (i < n4) qr[i] = quant4(v[j]);
         }
-        qr[i] = o;
+    } else {
+        for (int i = threadIdx.x; i < n4; i += kQuantThreads) qr[i] = quant4(xr[i]);
     }
+}
+
+// Launch of quant_act_kernel: the one-read build when the row fits 16
+// float4 per thread (K <= 16384), else the two-read build.
+void launch_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream) {
+    const int64_t nv = (K / 4 + kQuantThreads - 1) / kQuantThreads;
+    typedef void (*QFn)(const float *, int, int8_t *, float *);
+    QFn fn = quant_act_kernel<0>;
+    if (nv <= 1) fn = quant_act_kernel<1>;
+    else if (nv <= 2) fn = quant_act_kernel<2>;
+    else if (nv <= 4) fn = quant_act_kernel<4>;
+    else if (nv <= 8) fn = quant_act_kernel<8>;
+    else if (nv <= 16) fn = quant_act_kernel<16>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x, (int)K, xq, xs);
 }
 
 // --------------------------------------------------------------- tiled layout
@@ -2173,8 +2204,7 @@ int32_t s3d8_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *
     if (M > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "M too large");
     rc = check_device(nullptr);
     if (rc) return rc;
-    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(kQuantThreads), 0,
-                       (hipStream_t)stream, x, (int)K, xq, xs);
+    launch_quant_act(x, M, K, xq, xs, (hipStream_t)stream);
     return launch_status();
 }
 
