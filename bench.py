@@ -48,6 +48,7 @@ METRIC = "effective weight GB/s (% HBM peak) at M=1; INT8 TOPS (% MFMA peak) at 
 SETTLE_S = 0.2     # sustained load before the headline region (clock settle)
 NSAMPLES = 200     # per-call samples behind the median and its interval
 SAMPLE_REPS = 5    # replays of the R-step sequence per sample
+BUSY_REPS = 10     # R-step sequences queued ahead of the timed region
 
 # The pages' own throughput figures for this layer, all on Arm CPUs, quoted as
 # context (GMAC/s of the fused S3D8 kernel at m = 1, of the S3D8 -> INT8 path
@@ -211,12 +212,12 @@ def main():
     with torch.cuda.graph(graph):
         for r in range(R):
             step(r)
-    rem = args.steps % R
-    graph_rem = None
-    if rem:
-        graph_rem = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph_rem):
-            for r in range(rem):
+    # a longer untimed sequence that keeps the GPU busy while the host
+    # submits the timed steps (see below)
+    busy = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(busy):
+        for _ in range(BUSY_REPS):
+            for r in range(R):
                 step(r)
     torch.cuda.synchronize()
 
@@ -232,20 +233,23 @@ def main():
         torch.cuda.synchronize()
     log(f"timing {args.steps} steps (graph of {R} steps, R={R} weight copies)")
     # the timed region: exactly `steps` launches between two events on the
-    # launching stream.  One untimed replay is queued in front of the start
-    # event, after the synchronisation, so that the GPU is still busy with it
-    # while the host submits the timed launches: the region then holds the
-    # steps' GPU time and not the host's graph-launch latency (about 5 us per
-    # replay, which a region of only a few steps would otherwise carry).
+    # launching stream: steps // R replays of the R-step graph, then the
+    # remaining steps % R as direct calls.  An untimed sequence of BUSY_REPS
+    # * R steps is queued in front of the start event, after the
+    # synchronisation, so that the GPU is still busy with it while the host
+    # submits the timed launches: the region then holds the steps' GPU time
+    # and not host submission.  (Direct calls, not a graph, for the remainder:
+    # every graph replay carries a fixed cost of several microseconds, which a
+    # region of only a few steps would otherwise show.)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    graph.replay()
+    busy.replay()
     start.record()
     for i in range(args.steps // R):
         graph.replay()
-    if graph_rem is not None:
-        graph_rem.replay()
+    for r in range(args.steps % R):
+        step(r)
     end.record()
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
@@ -306,8 +310,8 @@ def main():
         log(f"variant {tag}: {v_us:.2f} us -> {variants['decode'][tag]['GBs']} GB/s effective weight bytes")
     # ---------------------------------------------------------------- c1 at M = 4 and 8
     # the other token counts of the c1 decode step: M = 4 through the same
-    # one-launch streaming kernel, M = 8 as quantisation plus the GEMV with
-    # the token rows as the MFMA's A operand (s3d8_forward picks both)
+    # one-launch streaming kernel, M = 8 as quantisation plus the streaming
+    # GEMV on the INT8 codes (s3d8_forward picks both)
     decode_m = {}
     for mm in (4, 8):
         lm_ = workloads.C1[mm]
@@ -320,7 +324,7 @@ def main():
         fns[0]()
         m_us = graph_launch_us(torch, fns, 10)
         decode_m[str(mm)] = {"us": round(m_us, 3), "GBs": round(weight_bytes / (m_us * 1e-6) / 1e9, 1),
-                             "path": "one streaming launch" if mm <= 4 else "quant_act + token-row GEMV"}
+                             "path": "one streaming launch" if mm <= 4 else "quant_act + streaming GEMV on the codes"}
         log(f"c1 decode M={mm}: {m_us:.2f} us -> {decode_m[str(mm)]['GBs']} GB/s effective weight bytes "
             f"({decode_m[str(mm)]['path']})")
         del xm_

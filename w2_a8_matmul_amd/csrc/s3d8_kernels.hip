@@ -712,6 +712,63 @@ struct StreamBatch {
     StreamProb p[kStreamBatch];
 };
 
+// The streaming kernels' decode table, built without staging it in LDS:
+// thread t of kThreads (1024) writes uint4 t + kThreads i (i < 4) of the
+// 64-copy table, entry b = t / 16 + 64 i.  For S3D8 all four entries use
+// centroid row (t / 32) % 32 (bits 1..5 of b come from t) and S0 = bit 4 of
+// t, while S1 and the bit-7 selector come from i; for 3D8 entry b is row b
+// of the 768-byte signed table.  Each thread loads the 8 bytes around its
+// row(s) from a 4-aligned offset (one row for S3D8, four for 3D8) with
+// asm loads that the caller waits for; build_stream_table then writes the
+// entries from registers.
+typedef uint32_t u2v_t __attribute__((ext_vector_type(2)));
+template <bool F3>
+struct StreamTableRows {
+    static constexpr int kRows = F3 ? kTabWords / 4 / 1024 : 1;
+    u2v_t cpair[kRows];
+    int cshift[kRows];
+};
+
+template <bool F3>
+__device__ __forceinline__ void load_stream_table_rows(StreamTableRows<F3> &t, const uint8_t *centroids, int tid) {
+    const v4i rcen = rsrc_words(centroids, F3 ? 768u : 96u);
+#pragma unroll
+    for (int k = 0; k < StreamTableRows<F3>::kRows; ++k) {
+        const int trow = F3 ? (tid >> 4) + k * (1024 >> 4) : ((tid >> 5) + k * (1024 >> 5)) & 31;
+        const int cbase = min((3 * trow) & ~3, F3 ? 760 : 88);
+        t.cshift[k] = 8 * (3 * trow - cbase);
+        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(t.cpair[k]) : "v"((uint32_t)cbase), "s"(rcen)
+                     : "memory");
+    }
+}
+
+template <bool F3>
+__device__ __forceinline__ void build_stream_table(uint32_t *tab, const StreamTableRows<F3> &t, int tid) {
+    constexpr int kThreads = 1024;
+    constexpr int kPasses = kTabWords / 4 / kThreads;
+    if constexpr (F3) {
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            const uint32_t v = (uint32_t)((((uint64_t)t.cpair[i].y << 32) | t.cpair[i].x) >> t.cshift[i]) & 0xFFFFFFu;
+            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
+        }
+    } else {
+        const bool s0 = (tid >> 4) & 1;
+        const uint64_t cv = (((uint64_t)t.cpair[0].y << 32) | t.cpair[0].x) >> t.cshift[0];
+        const uint32_t c0 = (uint32_t)cv & 0xFFu, c1 = (uint32_t)(cv >> 8) & 0xFFu, c2 = (uint32_t)(cv >> 16) & 0xFFu;
+        const uint32_t w0 = (s0 ? 0u - c0 : c0) & 0xFFu;
+        const uint32_t lo[2] = {w0 | (c1 << 8), w0 | (((0u - c1) & 0xFFu) << 8)};
+        const uint32_t hp = c2 << 16, hn = ((0u - c2) & 0xFFu) << 16;
+        const uint32_t hi[2] = {s0 ? hn : hp, s0 ? hp : hn};  // bit 7 clear: S2 = S0
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) {
+            const int hib = (kThreads / 16) * i;  // bits 6.. of b contributed by the pass
+            const uint32_t v = lo[(hib >> 6) & 1] | hi[(hib >> 7) & 1];
+            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
+        }
+    }
+}
+
 template <int MR, int W, int NF, bool F3>
 __device__ __forceinline__ void gemv_stream_body(
     const float *__restrict__ xf, const uint8_t *__restrict__ tiled, const uint8_t *__restrict__ centroids,
@@ -764,24 +821,10 @@ __device__ __forceinline__ void gemv_stream_body(
         ep_a[q] = __builtin_amdgcn_raw_buffer_load_b16(rsc, (idx < nout && ch < N) ? (uint32_t)ch * 2u : kOOB, 0, 0);
     }
 
-    // 2. the table rows of this thread's table entries (8 bytes from a
-    //    4-aligned offset inside the table each).  S3D8: entry b = idx / 16
-    //    of uint4 idx = tid + kThreads i uses centroid row (b / 2) % 32,
-    //    which takes kCenRows distinct values per thread.  3D8 (F3): entry b
-    //    is row b of the 768-byte signed table, one row per pass.
-    constexpr int kCenRows = 1024 / kThreads;
-    constexpr int kPasses = kTabWords / 4 / kThreads;
-    constexpr int kRows = F3 ? kPasses : kCenRows;
-    const v4i rcen = rsrc_words(centroids, F3 ? 768u : 96u);
-    u2v cpair[kRows];
-    int cshift[kRows];
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-        const int trow = F3 ? (tid >> 4) + k * (kThreads >> 4) : ((tid >> 5) + k * (kThreads >> 5)) & 31;
-        const int cbase = min((3 * trow) & ~3, F3 ? 760 : 88);
-        cshift[k] = 8 * (3 * trow - cbase);
-        asm volatile("buffer_load_dwordx2 %0, %1, %2, 0 offen" : "=v"(cpair[k]) : "v"((uint32_t)cbase), "s"(rcen) : "memory");
-    }
+    // 2. the table rows of this thread's table entries (load_stream_table_rows)
+    static_assert(W == 16, "the table build assumes 1024 threads");
+    StreamTableRows<F3> trows;
+    load_stream_table_rows<F3>(trows, centroids, tid);
 
     // 3. activations: this wave's K range of every row, up to 4 float4 per
     //    lane; float4 f of the range is row f / (16 kbw)
@@ -869,45 +912,13 @@ __device__ __forceinline__ void gemv_stream_body(
     if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
 
     // table: entry b holds [w0, w1, w2, 0] with w_d = +-C[q][d], q = (b >> 1)
-    // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0.
-    // Thread t writes uint4 t + 64 W i, entry b = t / 16 + 4 W i: bits 0..4
-    // of b come from t (t / 16 < 4 W <= 64), the rest from 4 W i, so S0 is
-    // fixed, q takes kCenRows values and S1, bit 7 depend on i only: every
-    // value is one of two low halves or-ed with one of two high halves of
-    // its centroid row.
-    static_assert(kCenRows * kThreads == 1024 && kPasses * kThreads == 4096, "table passes");
+    // % 32, sign selectors S0 = bit 0, S1 = bit 6, S2 = bit 7 xor bit 0
+    // (build_stream_table, from the rows loaded above).
     // (the empty statements after the wait keep every use of the rows behind it)
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly + NF) : "memory");
 #pragma unroll
-    for (int k = 0; k < kRows; ++k) asm volatile("" : "+v"(cpair[k]));
-    if constexpr (F3) {
-#pragma unroll
-        for (int i = 0; i < kPasses; ++i) {
-            const uint32_t v = (uint32_t)((((uint64_t)cpair[i].y << 32) | cpair[i].x) >> cshift[i]) & 0xFFFFFFu;
-            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
-        }
-    } else {
-        const bool s0 = (tid >> 4) & 1;
-        uint32_t lo[kCenRows][2], hi[kCenRows][2];
-#pragma unroll
-        for (int k = 0; k < kCenRows; ++k) {
-            const uint64_t cv = (((uint64_t)cpair[k].y << 32) | cpair[k].x) >> cshift[k];
-            const uint32_t c0 = (uint32_t)cv & 0xFFu, c1 = (uint32_t)(cv >> 8) & 0xFFu, c2 = (uint32_t)(cv >> 16) & 0xFFu;
-            const uint32_t w0 = (s0 ? 0u - c0 : c0) & 0xFFu;
-            lo[k][0] = w0 | (c1 << 8);
-            lo[k][1] = w0 | (((0u - c1) & 0xFFu) << 8);
-            const uint32_t hp = c2 << 16, hn = ((0u - c2) & 0xFFu) << 16;
-            hi[k][0] = s0 ? hn : hp;  // bit 7 clear: S2 = S0
-            hi[k][1] = s0 ? hp : hn;
-        }
-#pragma unroll
-        for (int i = 0; i < kPasses; ++i) {
-            constexpr int P = kThreads / 16;
-            const int hib = P * i;  // bits 5.. of b contributed by the pass
-            const uint32_t v = lo[(hib >> 5) & (kCenRows - 1)][(hib >> 6) & 1] | hi[(hib >> 5) & (kCenRows - 1)][(hib >> 7) & 1];
-            reinterpret_cast<uint4 *>(tab)[tid + kThreads * i] = make_uint4(v, v, v, v);
-        }
-    }
+    for (int k = 0; k < StreamTableRows<F3>::kRows; ++k) asm volatile("" : "+v"(trows.cpair[k]));
+    build_stream_table<F3>(tab, trows, tid);
 
     // activations landed (only fragment loads behind them)
     if constexpr (NF == 1) {
@@ -1153,6 +1164,258 @@ __global__ __launch_bounds__(W * 64) void gemv_stream_batch_kernel(const StreamB
     gemv_stream_body<MR, W, NF, false>(P.xf, P.tiled, P.centroids, P.scales, P.K, P.N,
                                        (int)blockIdx.x - B.wg0[pi], B.wg0[pi + 1] - B.wg0[pi], P.ntw_q, P.ntw_r,
                                        P.y, P.acc_out, P.xq_out, P.xs_out, 0);
+}
+
+// --------------------------------------------------------------- streaming GEMV on INT8 codes
+
+// The streaming GEMV's decode and sparse products for 1 to 8 token rows
+// whose INT8 codes and scales are already computed: s3d8_linear at M <= 8,
+// and s3d8_forward from five tokens on (after s3d8_quant_act, whose codes
+// every workgroup then reads instead of the fp32 rows).
+//
+// The sparse product v_smfmac_i32_16x16x128_i8 has 16 A rows; token r,
+// channel d takes row 3 r' + d of row group r / 5 (r' = r % 5), so five
+// tokens fill one group and six to eight tokens use two.  Both groups
+// multiply the same table-lookup dwords: the lookups, which dominate a
+// step, are shared, and a step runs two sparse products per group.  As in
+// the fused kernel the codes sit in LDS permuted in 8-byte chunks (code_pos)
+// so that one 16-byte read per lane is a group's A operand, and each lane
+// reads rows of its group only (others keep zeros); the weight fragments
+// stream through a ring of registers, kCodesSlots ahead.
+//
+// Work split as in the fused kernel: workgroup b takes tiles b, b + grid,
+// ... (at most kCodesMaxTiles), its 16 waves split K in ranges of kbw
+// 64-column blocks, partial sums meet in LDS through integer atomics.
+constexpr int kCodesMaxRows = 8;
+constexpr int kCodesWaveBytes = 4096;  // codes per wave: M * 64 * kbw <= 4096
+constexpr int kCodesMaxTiles = 16;
+constexpr int kCodesSlots = 4;
+
+template <int MR, int NCL, bool F3>
+__global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
+                                                          const uint8_t *__restrict__ tiled,
+                                                          const uint8_t *__restrict__ table,
+                                                          const uint16_t *__restrict__ scales, int K, int N,
+                                                          int ntw_q, int ntw_r, void *__restrict__ y,
+                                                          int32_t *__restrict__ acc_out, int obf) {
+    static_assert(MR >= 1 && MR <= kCodesMaxRows, "1 to 8 token rows");
+    static_assert(NCL >= 1 && NCL * 16 * 64 <= kCodesWaveBytes, "code loads per lane");
+    constexpr int W = 16, kThreads = W * 64;
+    constexpr int NG = MR > 5 ? 2 : 1;  // row groups of the sparse product (five tokens each)
+    constexpr int kEp = (kCodesMaxTiles * MR * 48 + kThreads - 1) / kThreads;
+    constexpr int kEarly = 2;           // ring entries issued before the first barrier
+    __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
+    // codes slice per wave: NCL loads of 16 bytes per lane, 1024 NCL bytes
+    __shared__ __attribute__((aligned(16))) int8_t xw[W][1024 * NCL];
+    __shared__ __attribute__((aligned(16))) int8_t zero16[16];
+    __shared__ int32_t ybuf[kCodesMaxTiles * MR * 48];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int T = (N + 2) / 3, KB = (K + 63) >> 6, tiles = (T + 15) >> 4;
+    const int kbw = (KB + W - 1) / W;
+    const int kb0 = wave * kbw;
+    const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
+    const int ntw = ntw_q + (bid < ntw_r);  // tiles of this workgroup, >= 1
+    const int nout = ntw * MR * 48;
+
+    // 1. epilogue operands (the compiler's loads, issued first: the explicit
+    //    vmcnt counts below never wait for them); output idx = tid + q *
+    //    kThreads is (tile j, row r, channel c)
+    const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales, (uint32_t)N * 2u);
+    uint16_t ep_a[kEp];
+    float ep_s[kEp];
+#pragma unroll
+    for (int q = 0; q < kEp; ++q) {
+        const int idx = tid + q * kThreads;
+        const int j = idx / (MR * 48), rc = idx - j * (MR * 48), r = rc / 48, c = rc - r * 48;
+        const int ch = (bid + j * grid) * 48 + c;
+        const bool ok = idx < nout && ch < N;
+        ep_a[q] = __builtin_amdgcn_raw_buffer_load_b16(rsc, ok ? (uint32_t)ch * 2u : kOOB, 0, 0);
+        ep_s[q] = ok ? xs[r] : 0.0f;
+    }
+
+    // 2. the small loads: this thread's table rows (load_stream_table_rows)
+    //    and this wave's codes, NCL 16-byte chunks per lane: chunk q of the
+    //    wave's slice is (row q / (4 kbw), columns 16 (q % (4 kbw)) ..)
+    StreamTableRows<F3> trows;
+    load_stream_table_rows<F3>(trows, reinterpret_cast<const uint8_t *>(table), tid);
+    const v4i rx = rsrc_words(xq, (uint32_t)MR * (uint32_t)K);
+    const int nq = MR * 4 * kbw;
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v cv[NCL];
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) {
+        const int q = lane + 64 * i;
+        const int r = q / (4 * kbw), c16 = q - r * 4 * kbw;
+        const int k = kb0 * 64 + 16 * c16;
+        const uint32_t off = (q < nq && k < K) ? (uint32_t)r * (uint32_t)K + (uint32_t)k : kOOB;
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "=v"(cv[i]) : "v"(off), "s"(rx) : "memory");
+    }
+    // every wave's small loads enter the CU's memory queue before any
+    // fragment load does
+    asm volatile("s_barrier" ::: "memory");
+
+    // 3. weight fragments into a ring of registers: step s of this wave =
+    //    tile j = s / kbw of the workgroup, block kb0 + s % kbw; steps past
+    //    the end read zeros.  Each entry is tied to its registers ("+v") and
+    //    waited for with vmcnt(slots - 1) before use (the younger loads are
+    //    the other entries).  kEarly entries now, the rest after the
+    //    workgroup barrier (a wave stalled issuing weight loads behind the
+    //    memory backlog would reach the barrier late).
+    const v4i rw = rsrc_words(tiled, (uint32_t)tiles * (uint32_t)KB * 1024u);
+    int is_j = 0, is_b = 0;  // (tile, block) of the next step to issue
+    auto next_off = [&]() {
+        const int kb = kb0 + is_b;
+        const bool live = is_j < ntw && kb < KB;
+        const uint32_t tile = (uint32_t)(bid + is_j * grid);
+        const uint32_t off = live ? (tile * (uint32_t)KB + (uint32_t)kb) * 1024u + (uint32_t)lane * 16u : kOOB;
+        if (++is_b == kbw) {
+            is_b = 0;
+            ++is_j;
+        }
+        return off;
+    };
+    u4v pr[kCodesSlots];
+    auto ring_load = [&](u4v &dst, uint32_t off) {
+        asm volatile("buffer_load_dwordx4 %0, %1, %2, 0 offen" : "+v"(dst) : "v"(off), "s"(rw) : "memory");
+    };
+#pragma unroll
+    for (int sl = 0; sl < kEarly; ++sl) {
+        asm volatile("" : "=v"(pr[sl]));
+        ring_load(pr[sl], next_off());
+    }
+
+    // 4. the table from the rows (only the codes and fragments may still be
+    //    in flight), then the codes (only fragments) into this wave's LDS
+    //    slice, 8-byte chunks at their permuted positions (read by this wave
+    //    only); the workgroup barrier completes the table and the zeroed sums
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly + NCL) : "memory");
+#pragma unroll
+    for (int k = 0; k < StreamTableRows<F3>::kRows; ++k) asm volatile("" : "+v"(trows.cpair[k]));
+    build_stream_table<F3>(tab, trows, tid);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kEarly) : "memory");
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) asm volatile("" : "+v"(cv[i]));
+#pragma unroll
+    for (int i = 0; i < NCL; ++i) {
+        const int q = lane + 64 * i;
+        if (q < nq) {
+            const int r = q / (4 * kbw), c16 = q - r * 4 * kbw;
+            int8_t *row = &xw[wave][r * 64 * kbw];
+            *reinterpret_cast<uint2 *>(row + code_pos(16 * c16)) = make_uint2(cv[i].x, cv[i].y);
+            *reinterpret_cast<uint2 *>(row + code_pos(16 * c16 + 8)) = make_uint2(cv[i].z, cv[i].w);
+        }
+    }
+    for (int i = tid; i < ntw * MR * 48; i += kThreads) ybuf[i] = 0;
+    if (tid < 4) reinterpret_cast<uint32_t *>(zero16)[tid] = 0u;
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int sl = kEarly; sl < kCodesSlots; ++sl) {
+        asm volatile("" : "=v"(pr[sl]));
+        ring_load(pr[sl], next_off());
+    }
+
+    // A operand of group gr: lane row arw = 3 r' + d holds token 5 gr + r'
+    // (rows past the tokens read zeros); sparsity index words as in the
+    // fused kernel (the first product sends the even code bytes to position
+    // d and the odd ones to position 3, a zero of every table dword; the
+    // second the reverse)
+    const int arw = lane & 15;
+    const uint32_t dsel = (uint32_t)(arw % 3);
+    const int idx_even = (int)(dsel * 0x11111111u + 0xCCCCCCCCu);
+    const int idx_odd = (int)(0x33333333u + dsel * 0x44444444u);
+    const int8_t *xa[NG];
+    int xa_step[NG];
+    bool arow[NG];
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+        const int tok = 5 * gr + arw / 3;
+        arow[gr] = arw < 15 && tok < MR;
+        xa[gr] = arow[gr] ? &xw[wave][tok * 64 * kbw + g * 16] : zero16;
+        xa_step[gr] = arow[gr] ? 64 : 0;
+    }
+    const uint32_t lane_off = (uint32_t)lane << 2;
+    const char *tb = reinterpret_cast<const char *>(tab);
+    const int nsteps = ntw * kbw;
+
+    v4i acc[NG], a[NG];
+#pragma unroll
+    for (int gr = 0; gr < NG; ++gr) {
+        acc[gr] = v4i{0, 0, 0, 0};
+        a[gr] = v4i{0, 0, 0, 0};
+    }
+    int bl = 0, j = 0;
+#pragma unroll 1
+    for (int st0 = 0; st0 < nsteps; st0 += kCodesSlots) {
+#pragma unroll
+        for (int u = 0; u < kCodesSlots; ++u) {
+            if (st0 + u >= nsteps) break;  // uniform
+            asm volatile("s_waitcnt vmcnt(%1)" : "+v"(pr[u]) : "n"(kCodesSlots - 1) : "memory");
+            const u4v p = pr[u];
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr)
+                if (arow[gr]) a[gr] = *reinterpret_cast<const v4i *>(xa[gr] + bl * xa_step[gr]);
+            const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+            v8i be, bo;  // table dwords of the lane's even / odd bytes
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int32_t t = *reinterpret_cast<const int32_t *>(
+                        tb + __builtin_amdgcn_perm(pw[jj], lane_off, 0x0C0C0400u + ((uint32_t)i << 8)));
+                    if (i & 1)
+                        bo[2 * jj + (i >> 1)] = t;
+                    else
+                        be[2 * jj + (i >> 1)] = t;
+                }
+            }
+#pragma unroll
+            for (int gr = 0; gr < NG; ++gr) {
+                acc[gr] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[gr], be, acc[gr], idx_even, 0, 0);
+                acc[gr] = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a[gr], bo, acc[gr], idx_odd, 0, 0);
+            }
+            ring_load(pr[u], next_off());
+            if (++bl == kbw) {
+                // tile j done for this wave: lane (n, g) holds rows 4 g + i of
+                // each group, row 3 r' + d = channel 3 n + d of token 5 gr + r'
+                if (kb0 < KB) {
+#pragma unroll
+                    for (int gr = 0; gr < NG; ++gr)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int m = 4 * g + i, tok = 5 * gr + m / 3;
+                            if (m < 15 && tok < MR) atomicAdd(&ybuf[(j * MR + tok) * 48 + 3 * n + m % 3], acc[gr][i]);
+                        }
+                }
+#pragma unroll
+                for (int gr = 0; gr < NG; ++gr) acc[gr] = v4i{0, 0, 0, 0};
+                bl = 0;
+                ++j;
+            }
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // (the ring registers stay allocated until every load into them landed)
+#pragma unroll
+    for (int sl = 0; sl < kCodesSlots; ++sl) asm volatile("" ::"v"(pr[sl]));
+
+#pragma unroll
+    for (int q = 0; q < kEp; ++q) {
+        const int idx = tid + q * kThreads;
+        const int jj = idx / (MR * 48), rc = idx - jj * (MR * 48), r = rc / 48, c = rc - r * 48;
+        const int ch = (bid + jj * grid) * 48 + c;
+        if (idx < nout && ch < N) {
+            const int32_t sum = ybuf[(jj * MR + r) * 48 + c];
+            const float v = (ep_s[q] * (float)sum) * bf16_to_f32(ep_a[q]);
+            if (obf)
+                static_cast<uint16_t *>(y)[(int64_t)r * N + ch] = f32_to_bf16_rne(v);
+            else
+                static_cast<float *>(y)[(int64_t)r * N + ch] = v;
+            if (acc_out) acc_out[(int64_t)r * N + ch] = sum;
+        }
+    }
 }
 
 // --------------------------------------------------------------- GEMM
@@ -2183,6 +2446,37 @@ bool launch_gemv_stream_batch(int count, const s3d8_forward_item *items, int cus
     return true;
 }
 
+// The streaming GEMV on INT8 codes (gemv_codes_kernel) for 1 to 8 token
+// rows: taken when every wave's codes fit its LDS slice (M * 64 * kbw <=
+// 4096 bytes, kbw = ceil(ceil(K/64) / 16)) and no workgroup needs more than
+// kCodesMaxTiles tiles (one workgroup per CU).  Returns false, launching
+// nothing, otherwise.
+bool launch_gemv_codes(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                       const void *table, bool f3d8, const uint16_t *scales, void *y, bool obf, int32_t *acc_out,
+                       int cus, hipStream_t stream) {
+    if (M < 1 || M > kCodesMaxRows) return false;
+    const int64_t KB = (K + 63) / 64, kbw = (KB + 15) / 16;
+    if (M * 64 * kbw > kCodesWaveBytes) return false;
+    const int64_t tiles = ((N + 2) / 3 + 15) / 16;
+    const int64_t grid = tiles < cus ? tiles : cus;
+    if ((tiles + grid - 1) / grid > kCodesMaxTiles) return false;
+    typedef void (*CodesFn)(const int8_t *, const float *, const uint8_t *, const uint8_t *, const uint16_t *, int,
+                            int, int, int, void *, int32_t *, int);
+    // 16-byte code loads per lane: M * 4 * kbw chunks over 64 lanes (1, 2 or 4)
+    const int64_t ncl = (M * 4 * kbw + 63) / 64;
+    const int cl = ncl <= 1 ? 0 : ncl <= 2 ? 1 : 2;
+#define S3D8_CODES(m, f) {gemv_codes_kernel<m, 1, f>, gemv_codes_kernel<m, 2, f>, gemv_codes_kernel<m, 4, f>}
+#define S3D8_CODES_ROWS(f) {S3D8_CODES(1, f), S3D8_CODES(2, f), S3D8_CODES(3, f), S3D8_CODES(4, f), \
+                            S3D8_CODES(5, f), S3D8_CODES(6, f), S3D8_CODES(7, f), S3D8_CODES(8, f)}
+    static const CodesFn fns[2][kCodesMaxRows][3] = {S3D8_CODES_ROWS(false), S3D8_CODES_ROWS(true)};
+#undef S3D8_CODES_ROWS
+#undef S3D8_CODES
+    hipLaunchKernelGGL(fns[f3d8 ? 1 : 0][M - 1][cl], dim3((unsigned)grid), dim3(1024), 0, stream, xq, xs, tiled,
+                       static_cast<const uint8_t *>(table), scales, (int)K, (int)N, (int)(tiles / grid),
+                       (int)(tiles % grid), y, acc_out, (int)obf);
+    return true;
+}
+
 bool launch_gemv_stream(const float *x, int8_t *xq, float *xs, int64_t M, int64_t K, int64_t N,
                         const uint8_t *tiled, const uint8_t *centroids, const uint16_t *scales, void *y,
                         int32_t *acc_out, int cus, hipStream_t stream, bool f3d8, int obf) {
@@ -2295,7 +2589,11 @@ int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
                            acc_out, nbm, nbn, (int)f3d8);
         return launch_status();
     }
-    // the GEMV takes up to 16 token rows per launch
+    // up to 8 token rows: the streaming GEMV on the codes, when they fit it
+    if (launch_gemv_codes(xq, xs, M, K, N, tiled, table, f3d8, scales_bf16, y, obf, acc_out, cus,
+                          (hipStream_t)stream))
+        return launch_status();
+    // otherwise the token-row GEMV, up to 16 token rows per launch
     const size_t ysize = obf ? 2 : 4;
     for (int64_t m0 = 0; m0 < M; m0 += 16) {
         const int mrows = (int)(M - m0 < 16 ? M - m0 : 16);
