@@ -345,6 +345,48 @@ int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, 
                        int64_t tiled_bytes, const void *table, int32_t format, const uint16_t *scales_bf16, void *y,
                        int32_t out_type, int32_t *acc_out, void *stream);
 
+/* Split-K form of s3d8_linear_ex, for prefill shapes with few output tiles
+ * and long rows, such as the vision encoder's MLP down-projection
+ * (K = 5120, N = 1280 at 1601 tokens; [PAPER] Sec. 4.3, Table 2): the fused
+ * GEMM for M > 16 with its input columns cut into `splits` ranges of whole
+ * 64-column blocks, one workgroup per (output tile, range).  The ranges'
+ * INT32 partial sums are added exactly before the epilogue ([BLOG] "Fused
+ * matrix-vector product": accumulate in INT32, then scale), so results are
+ * identical to s3d8_linear_ex for every split count.  M <= 16 runs the
+ * GEMV paths of s3d8_linear_ex (no split, workspace unused).
+ *   splits     ranges per tile: 0 = s3d8_splitk_auto for the current device;
+ *              otherwise at least 1, clamped to ceil(K/64) and rounded so
+ *              that no range is empty.
+ *   workspace  device, 256-B aligned, at least
+ *              s3d8_splitk_workspace_bytes(M, K, N, splits) bytes (splits as
+ *              resolved for 0), owned by the caller; NULL allowed when that
+ *              size is 0.  It holds two counters per output tile and the
+ *              partial sums.  It must be filled with zeros once before its
+ *              first use; every call leaves the counters at zero again, so
+ *              later calls need no clearing.  Calls that may run
+ *              concurrently need separate workspaces.
+ *   workspace_bytes  its size.
+ *   the rest   as for s3d8_linear_ex.
+ * Errors: as s3d8_linear_ex; INVALID_ARG also for splits < 0 or a missing
+ * or too small workspace; ALIGN for a misaligned workspace; SHAPE also when
+ * the partial sums would exceed 2^31 bytes. */
+int32_t s3d8_linear_splitk(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                           int64_t tiled_bytes, const void *table, int32_t format, const uint16_t *scales_bf16,
+                           void *y, int32_t out_type, int32_t *acc_out, int32_t splits, void *workspace,
+                           int64_t workspace_bytes, void *stream);
+
+/* The split count s3d8_linear_splitk takes for splits = 0 on a GPU with
+ * num_cus compute units: the S that minimises ceil(ceil(K/64)/S) + 9 S
+ * (the main loop's 64-column blocks per workgroup plus the measured cost of
+ * adding S slots of partial sums, in the same unit) among 1 and the counts
+ * whose workgroups fit one round on the CUs (output tiles x S <= num_cus),
+ * at most 16.  1 for M <= 16.  -1 on bad sizes. */
+int32_t s3d8_splitk_auto(int64_t M, int64_t K, int64_t N, int32_t num_cus);
+
+/* Workspace bytes of s3d8_linear_splitk at a split count >= 1 (0 for M <= 16
+ * or a single range).  -1 on bad sizes. */
+int64_t s3d8_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t splits);
+
 /* s3d8_forward for either weight format and either output type (arguments
  * as s3d8_linear_ex and s3d8_forward; xq and xs as for s3d8_forward).  The
  * same launches as s3d8_forward.  Errors: as s3d8_forward, plus

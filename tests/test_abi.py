@@ -347,3 +347,78 @@ def test_variant_entry_points_validation():
     assert L.s3d8_dequant_ex(A16, None, 1, 9, 64, A16, None) == _lib.S3D8_ERR_INVALID_ARG
     assert L.s3d8_dequant_ex(A16, A16 + 2, 1, 9, 64, A16, None) == _lib.S3D8_ERR_ALIGN
     assert L.s3d8_dequant_ex(A16, A16, 1, 9, 24, A16, None) == _lib.S3D8_ERR_SHAPE
+
+
+def _splitk_bytes_closed_form(M, K, N, splits):
+    """Two int32 counters per output tile (padded to 256 bytes) plus, per
+    tile, `splits` slots of 4 waves x 3 RT accumulators x 64 lanes x 16
+    int32; the larger need of the two tile heights (RT = 4, 5 rows of 32)."""
+    T = -(-N // 3)
+    KB = -(-K // 64)
+    s = max(1, min(splits, KB))
+    kbper = -(-KB // s)
+    s = -(-KB // kbper)
+    if M <= 16 or s == 1:
+        return 0
+    best = 0
+    for rt in (4, 5):
+        tiles = -(-M // (32 * rt)) * -(-(-(-T // 16)) // 8)
+        best = max(best, -(-(8 * tiles) // 256) * 256 + tiles * s * 4 * 3 * rt * 64 * 16 * 4)
+    return best
+
+
+@pytest.mark.parametrize("M,K,N,splits", [(1601, 5120, 1280, 4), (1601, 1280, 5120, 2), (2048, 4096, 14336, 3),
+                                          (300, 1040, 772, 5), (17, 80, 50, 7), (33, 640, 97, 4),
+                                          (33, 640, 97, 6), (1601, 5120, 1280, 1)])
+def test_splitk_workspace_bytes(M, K, N, splits):
+    L = _lib.lib()
+    assert L.s3d8_splitk_workspace_bytes(M, K, N, splits) == _splitk_bytes_closed_form(M, K, N, splits)
+
+
+def test_splitk_sizes_and_choice():
+    L = _lib.lib()
+    # worked case: the vision MLP down-projection at 1601 tokens needs 13 x 4
+    # tiles of 128 rows x 384 channels (52 of 256 CUs) and has 80 column
+    # blocks: ceil(80/S) + 9 S is 89, 58, 54, 56 for S = 1..4, so 3 ranges;
+    # its workspace at 4 (RT = 5 is the larger: 11 x 4 tiles)
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 256) == 3
+    assert L.s3d8_splitk_workspace_bytes(1601, 5120, 1280, 4) == 512 + 44 * 4 * 4 * 61440
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 104) == 2  # 3 x 52 tiles would not fit one round
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 103) == 1
+    assert L.s3d8_splitk_auto(1601, 1280, 5120, 256) == 1  # up-projection: 182 tiles
+    assert L.s3d8_splitk_auto(2048, 4096, 14336, 256) == 1
+    assert L.s3d8_splitk_auto(16, 5120, 1280, 256) == 1    # GEMV path
+    assert L.s3d8_splitk_auto(17, 12800, 96, 256) == 5     # 200 blocks: 40 + 45 < 50 + 36
+    assert L.s3d8_splitk_auto(17, 64 * 4000, 96, 256) == 16  # at most 16 ranges
+    assert L.s3d8_splitk_auto(17, 256, 96, 256) == 1       # 4 blocks: no split
+    assert L.s3d8_splitk_auto(0, 64, 9, 256) == -1
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 0) == -1
+    assert L.s3d8_splitk_workspace_bytes(16, 5120, 1280, 4) == 0
+    assert L.s3d8_splitk_workspace_bytes(1601, 5120, 1280, 0) == -1
+    assert L.s3d8_splitk_workspace_bytes(17, 80, 50, 1) == 0
+    # ranges are rounded so that none is empty: 10 blocks in 6 requested
+    # ranges become 5 ranges of 2
+    assert L.s3d8_splitk_workspace_bytes(33, 640, 97, 6) == L.s3d8_splitk_workspace_bytes(33, 640, 97, 5)
+
+
+def test_splitk_validation():
+    L = _lib.lib()
+    M, K, N = 1601, 5120, 1280
+    need = L.s3d8_splitk_workspace_bytes(M, K, N, 4)
+
+    def call(ws=A16, nbytes=need, splits=4, fmt=0, out=0, xq=A16, M=M, N=N):
+        return L.s3d8_linear_splitk(xq, A16, M, K, N, A16, TB, A16, fmt, A16, A16, out, None, splits, ws, nbytes,
+                                    None)
+
+    assert call(splits=-1) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(ws=None) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(nbytes=need - 1) == _lib.S3D8_ERR_INVALID_ARG
+    assert b"workspace" in L.s3d8_last_error()
+    assert call(ws=A16 + 16) == _lib.S3D8_ERR_ALIGN
+    assert call(xq=A_ODD) == _lib.S3D8_ERR_ALIGN
+    assert call(fmt=2) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(out=5) == _lib.S3D8_ERR_INVALID_ARG
+    assert call(N=3355443 * 3) == _lib.S3D8_ERR_SHAPE
+    # partial sums over 2^31 bytes
+    assert call(M=100000, N=12800, nbytes=1 << 40) == _lib.S3D8_ERR_SHAPE
+    assert b"partial" in L.s3d8_last_error()

@@ -8,9 +8,10 @@ M = 1601 tokens.  Weights are the oracle-packed matrices of the parity inputs
 (tests/golden/centroids.json tables, the oracle's frozen-centroid encoder),
 activations the seeded N(0, 1) draws.
 
-Each configuration runs through both prefill paths (the fused GEMM of
-s3d8_linear and the decode-then-INT8-GEMM of s3d8_linear_unfused) in three
-modes: with the INT32 accumulators requested, and without them (the kernel
+Each configuration runs through the three prefill paths (the fused GEMM of
+s3d8_linear, the decode-then-INT8-GEMM of s3d8_linear_unfused, and the
+split-K fused GEMM of s3d8_linear_splitk with the library's split count, as
+the benchmark runs it) in three modes: with the INT32 accumulators requested, and without them (the kernel
 builds the benchmark times, which never store accumulators) with fp32 and
 with bf16 output.  Every output is compared: accumulators bit-exact, fp32
 outputs bit-identical to the oracle's epilogue (the 1e-6 relative bar is
@@ -18,8 +19,12 @@ checked as well), bf16 outputs equal to the oracle's round-to-nearest-even of
 its fp32 outputs.
 
 The same three modes run on ragged shapes (row, triple and K tails, both
-row-tile heights) and through s3d8_forward, whose small-M kernels are also
-built separately for the accumulator-free case.
+row-tile heights; split-K into 3 ranges) and through s3d8_forward, whose
+small-M kernels are also built separately for the accumulator-free case.
+Split-K is also run at the full prefill sizes with explicit split counts,
+over a sweep of split counts on a ragged shape (ranges of unequal length,
+one block per range, more ranges than blocks), and with one workspace
+reused across calls (its counters must return to zero).
 """
 import functools
 
@@ -72,11 +77,18 @@ def _oracle_full(name):
 
 
 def _run_prefill(gpu, path, mode, x, C, alpha, packed, N):
-    """One call of s3d8_linear / s3d8_linear_unfused; returns (xq, xs, acc or
-    None, y as numpy: fp32, or bf16 bit patterns)."""
+    """One call of s3d8_linear / s3d8_linear_unfused / s3d8_linear_splitk
+    ("splitk": the library's split count, "splitk<S>": S ranges); returns
+    (xq, xs, acc or None, y as numpy: fp32, or bf16 bit patterns)."""
     xq, xs = s3d8.quant_act(dev(x, gpu))
     tiled = s3d8.tile(dev(packed, gpu), N)
-    fn = s3d8.linear if path == "fused" else s3d8.linear_unfused
+    if path.startswith("splitk"):
+        splits = int(path[6:] or 0)
+
+        def fn(*a, **k):
+            return s3d8.linear_splitk(*a, splits=splits, **k)
+    else:
+        fn = s3d8.linear if path == "fused" else s3d8.linear_unfused
     out = "bf16" if mode == "y_bf16" else "f32"
     if mode == "acc":
         y, acc = fn(xq, xs, tiled, dev(C, gpu), dev(alpha.view(np.int16), gpu), N, return_acc=True)
@@ -100,7 +112,7 @@ def _compare(got, ref_xq, ref_xs, ref_acc, ref_y, mode):
 
 
 @pytest.mark.parametrize("mode", ["acc", "y_f32", "y_bf16"])
-@pytest.mark.parametrize("path", ["fused", "unfused"])
+@pytest.mark.parametrize("path", ["fused", "unfused", "splitk"])
 @pytest.mark.parametrize("name", list(PREFILL))
 def test_prefill_full_output_matches_oracle(gpu, name, path, mode):
     lin = PREFILL[name]
@@ -118,8 +130,20 @@ RAGGED = [(1270, 80, 12280), (2000, 1024, 14335), (300, 1040, 772), (33, 1040, 9
           (16, 1040, 97), (9, 256, 48), (5, 64, 47), (1, 4096, 300)]
 
 
+@pytest.mark.parametrize("name,splits", [("vision_down", 2), ("vision_down", 3), ("vision_down", 5),
+                                         ("vision_up", 2), ("vision_up", 4), ("c3", 2)])
+def test_splitk_full_output_matches_oracle(gpu, name, splits):
+    """Split-K at the full prefill sizes with explicit split counts (vision
+    down: 80 blocks in 2, 3 or 5 ranges; vision up: 20 blocks; c3 on
+    160-row tiles), accumulators and fp32 outputs in full."""
+    lin = PREFILL[name]
+    x, C, alpha, packed, xq_r, xs_r, acc_r, y_r = _oracle_full(name)
+    got = _run_prefill(gpu, "splitk%d" % splits, "acc", x, C, alpha, packed, lin.N)
+    _compare(got, xq_r, xs_r, acc_r, y_r, "acc")
+
+
 @pytest.mark.parametrize("mode", ["acc", "y_f32", "y_bf16"])
-@pytest.mark.parametrize("path", ["fused", "unfused"])
+@pytest.mark.parametrize("path", ["fused", "unfused", "splitk3"])
 @pytest.mark.parametrize("M,K,N", RAGGED)
 def test_linear_modes_ragged(gpu, M, K, N, path, mode):
     C, alpha, packed = random_format([4000, M, K, N], N, K)
@@ -160,3 +184,52 @@ def test_forward_modes(gpu, M, K, N, mode):
         np.testing.assert_array_equal(bf16_bits(y), oracle.to_bf16(y_r))
     else:
         check_y(y.cpu().numpy(), y_r)
+
+
+# K = 1040: 17 column blocks, the last one ragged (16 columns)
+@pytest.mark.parametrize("splits", [2, 3, 4, 5, 7, 16, 17, 40])
+@pytest.mark.parametrize("M,N", [(300, 772), (1270, 97), (33, 12280)])
+def test_splitk_split_counts(gpu, M, N, splits):
+    """Every split count on a ragged K: unequal ranges, one block per range
+    (17), more ranges requested than blocks (40 is clamped to 17), both
+    row-tile heights."""
+    K = 1040
+    C, alpha, packed = random_format([4020, M, K, N], N, K)
+    x = workloads.gaussian_matrix([4021, M, K], M, K)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    got = _run_prefill(gpu, "splitk%d" % splits, "acc", x, C, alpha, packed, N)
+    _compare(got, xq_r, xs_r, acc_r, y_r, "acc")
+
+
+def test_splitk_workspace_reuse(gpu):
+    """One zero-filled workspace across calls of different shapes and split
+    counts: every result matches the oracle, and the per-tile counters are
+    back at zero after each call."""
+    ws = torch.zeros((s3d8.splitk_workspace_bytes(300, 5120, 1280, 5),), dtype=torch.uint8, device=gpu)
+    for i, (M, K, N, splits) in enumerate([(300, 5120, 1280, 5), (300, 5120, 1280, 5), (200, 1040, 772, 3),
+                                           (300, 5120, 1280, 4), (40, 640, 97, 2)]):
+        C, alpha, packed = random_format([4030, i], N, K)
+        x = workloads.gaussian_matrix([4031, i], M, K)
+        xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+        xq, xs = s3d8.quant_act(dev(x, gpu))
+        tiled = s3d8.tile(dev(packed, gpu), N)
+        y, acc = s3d8.linear_splitk(xq, xs, tiled, dev(C, gpu), dev(alpha.view(np.int16), gpu), N, splits=splits,
+                                    workspace=ws, return_acc=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+        check_y(y.cpu().numpy(), y_r)
+        # the counters (two int32 per tile, at most 12 tiles here) and their
+        # padding fill the first 256 bytes; the partial sums follow
+        assert int(ws[:256].count_nonzero()) == 0
+
+
+def test_splitk_small_m_takes_gemv(gpu):
+    """M <= 16 through s3d8_linear_splitk is the GEMV path of s3d8_linear
+    (no workspace needed), identical results."""
+    M, K, N = 8, 4096, 1000
+    C, alpha, packed = random_format([4040], N, K)
+    x = workloads.gaussian_matrix([4041], M, K)
+    xq_r, xs_r, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    assert s3d8.splitk_workspace_bytes(M, K, N, 4) == 0
+    got = _run_prefill(gpu, "splitk4", "acc", x, C, alpha, packed, N)
+    _compare(got, xq_r, xs_r, acc_r, y_r, "acc")

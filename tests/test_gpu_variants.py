@@ -5,8 +5,8 @@ whole byte indexes a (256, 3) table of signed values) and bfloat16 outputs
 (blog "Fused matrix-vector product": results are converted to bf16 on the way
 out), through every kernel path: the streaming GEMV (M <= 4), the fused GEMV
 fallback, the GEMV on pre-quantised activations (M <= 16), the fused GEMM
-(both row-tile variants), the unfused decode + INT8 GEMM and the standalone
-dequantisation.
+(both row-tile variants, whole and split-K), the unfused decode + INT8 GEMM
+and the standalone dequantisation.
 
 Bar: codes, scales, decoded weights and INT32 accumulators bit-exact; fp32
 outputs bit-identical to the oracle (within 1e-6 relative at worst); bf16
@@ -68,6 +68,9 @@ def run(kind, x, table, alpha, packed, N, gpu, fmt, out):
     s = dev(alpha.view(np.int16), gpu)
     if kind == "forward":
         y, xq, xs, acc = s3d8.forward(dev(x, gpu), tiled, t, s, N, return_all=True, fmt=fmt, out=out)
+    elif kind == "splitk":
+        xq, xs = s3d8.quant_act(dev(x, gpu))
+        y, acc = s3d8.linear_splitk(xq, xs, tiled, t, s, N, splits=3, return_acc=True, fmt=fmt, out=out)
     else:
         xq, xs = s3d8.quant_act(dev(x, gpu))
         fn = s3d8.linear if kind == "linear" else s3d8.linear_unfused
@@ -109,12 +112,14 @@ def test_dequant_3d8_every_byte_value(gpu):
 # (kind, M, K, N): forward at M <= 4 is the streaming GEMV; at N = 200000
 # (over 16 tiles per CU) the fused GEMV; M = 4 with K = 5120 and M = 8 run
 # quantisation then the GEMV on quantised activations (as linear at M <= 16);
-# M = 40 / 300 the fused GEMM (row tiles of 128 and 160).
+# M = 40 / 300 the fused GEMM (row tiles of 128 and 160), also split into 3
+# column-block ranges (split-K).
 PATHS = [
     ("forward", 1, 256, 384), ("forward", 2, 1040, 97), ("forward", 3, 4096, 50), ("forward", 4, 64, 47),
     ("forward", 1, 64, 200000), ("forward", 4, 5120, 101), ("forward", 8, 1280, 98), ("linear", 1, 80, 50),
     ("linear", 16, 1040, 97),
     ("linear", 40, 256, 385), ("linear", 300, 1040, 772), ("unfused", 40, 1040, 97), ("unfused", 129, 256, 385),
+    ("splitk", 40, 1040, 97), ("splitk", 300, 1040, 772),
 ]
 
 

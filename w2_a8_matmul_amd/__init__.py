@@ -25,6 +25,7 @@ __all__ = [
     "S3D8Error", "num_triples", "packed_bytes", "format_bytes", "tiled_bytes", "pack", "encode",
     "tile", "quant_act", "linear", "linear_unfused", "unfused_workspace_bytes", "forward", "dequant",
     "PackedLinear", "hbm_read_probe", "mfma_rate_probe", "encode_device", "forward_batch",
+    "linear_splitk", "splitk_auto", "splitk_workspace_bytes",
 ]
 
 
@@ -265,6 +266,49 @@ def linear_unfused(xq, xs, tiled, centroids, scales, N: int, workspace=None, y=N
             call("s3d8_linear_unfused", *args, scales.data_ptr(), y.data_ptr(), *tail)
         else:
             call("s3d8_linear_unfused_ex", *args, f, scales.data_ptr(), y.data_ptr(), o, *tail)
+    if return_acc:
+        return y, acc
+    return y
+
+
+def splitk_auto(M: int, K: int, N: int, num_cus: int) -> int:
+    return int(lib().s3d8_splitk_auto(M, K, N, num_cus))
+
+
+def splitk_workspace_bytes(M: int, K: int, N: int, splits: int) -> int:
+    return int(lib().s3d8_splitk_workspace_bytes(M, K, N, splits))
+
+
+def linear_splitk(xq, xs, tiled, centroids, scales, N: int, splits: int = 0, workspace=None, y=None, acc=None,
+                  return_acc: bool = False, fmt: str = "s3d8", out: str = "f32"):
+    """Same result as ``linear``, with the fused GEMM's input columns split
+    into ``splits`` ranges whose INT32 partial sums are added before the
+    epilogue (0: the library's choice for this GPU).  The workspace holds the
+    partial sums and per-tile counters; it is allocated here, zero-filled,
+    unless given (a given one must have been zero-filled before its first
+    use; each call leaves it ready for the next)."""
+    torch = _torch()
+    f, o = _variant(fmt, out)
+    _dev_check(xq, torch.int8, "xq")
+    M, K = xq.shape
+    _dev_check(xs, torch.float32, "xs", xq.device, min_numel=M)
+    scales = _scales_view(scales)
+    _check_weights(tiled, centroids, scales, N, K, fmt, xq.device)
+    if splits == 0:
+        splits = splitk_auto(M, K, N, torch.cuda.get_device_properties(xq.device).multi_processor_count)
+    if splits < 1:
+        raise ValueError("splits must be 0 (automatic) or positive")
+    wbytes = splitk_workspace_bytes(M, K, N, splits)
+    if workspace is None:
+        workspace = torch.zeros((max(wbytes, 1),), dtype=torch.uint8, device=xq.device)
+    _dev_check(workspace, torch.uint8, "workspace", xq.device, min_numel=wbytes)
+    y = _y_out(y, M, N, out, xq.device)
+    acc = _acc_out(acc, return_acc, M, N, xq.device)
+    with torch.cuda.device(xq.device):
+        call("s3d8_linear_splitk", xq.data_ptr(), xs.data_ptr(), M, K, N, tiled.data_ptr(), tiled.numel(),
+             centroids.data_ptr(), f, scales.data_ptr(), y.data_ptr(), o,
+             acc.data_ptr() if acc is not None else None, splits, workspace.data_ptr(), workspace.numel(),
+             _stream(xq))
     if return_acc:
         return y, acc
     return y

@@ -52,6 +52,10 @@ SIGNATURES = {
     "s3d8_mfma_rate_probe": (_I32, [_I32, _I32, _I32, _P, _P]),
     "s3d8_hbm_read_probe": (_I32, [_P, _I64, _I32, _P, _P]),
     "s3d8_linear_unfused_noalloc": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _P, _P, _P, _P]),
+    "s3d8_linear_splitk": (_I32, [_P, _P, _I64, _I64, _I64, _P, _I64, _P, _I32, _P, _P, _I32, _P, _I32, _P, _I64,
+                                  _P]),
+    "s3d8_splitk_auto": (_I32, [_I64, _I64, _I64, _I32]),
+    "s3d8_splitk_workspace_bytes": (_I64, [_I64, _I64, _I64, _I32]),
 }
 
 

@@ -327,7 +327,7 @@ void clear_error() { g_last_error.clear(); }
 
 extern "C" {
 
-int32_t s3d8_version(void) { return 20000; }
+int32_t s3d8_version(void) { return 20100; }
 
 int64_t s3d8_num_triples(int64_t N) { return N > 0 ? (N + 2) / 3 : -1; }
 

@@ -33,6 +33,7 @@
 namespace {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef int32_t v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kTabEntries = 256;
@@ -1462,17 +1463,27 @@ typedef int32_t v16i __attribute__((ext_vector_type(16)));
 // about 8 row blocks x 4 column blocks, so their activation and weight
 // tiles are shared through that XCD's L2 instead of each workgroup
 // streaming its own weight stripe.
+//
+// With the input columns split into `splits` ranges, the range index ks is
+// the slowest: an XCD's workgroups then share a k range as well.
 constexpr int kGroupM = 8;
-__device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
-    const int nwg = nbm * nbn;
+__device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int splits, int &bm, int &bn, int &ks) {
+    const int nt = nbm * nbn;
+    const int nwg = nt * splits;
     const int per_xcd = (nwg + kXcds - 1) / kXcds;
-    const int L = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-    if (L >= nwg) return false;
+    const int L0 = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (L0 >= nwg) return false;
+    ks = L0 / nt;
+    const int L = L0 - ks * nt;
     const int group = L / (kGroupM * nbn), r = L - group * (kGroupM * nbn);
     const int gm = min(kGroupM, nbm - group * kGroupM);
     bm = group * kGroupM + r % gm;
     bn = r / gm;
     return true;
+}
+__device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
+    int ks;
+    return gemm_tile(nbm, nbn, 1, bm, bn, ks);
 }
 
 // s_waitcnt vmcnt(N) for the loads the compiler does not see (LDS-DMA), and
@@ -1607,12 +1618,44 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
     }
 }
 
-template <int RT, bool kAcc, bool kBF>
+// Split-K (splits > 1): the ceil(K/64) column blocks are cut into ranges of
+// kbper blocks and workgroup (tile, ks) runs range ks only.  Its INT32 sums
+// are exact partial sums of the tile's accumulators, so adding the ranges'
+// sums in any order gives the accumulators of the whole product.  The
+// workgroups of a tile meet through two counters per tile in ws_cnt: each
+// takes an arrival number from the first and stores its partial sums in slot
+// `arrival` of the tile in ws_part (`splits` slots per tile,
+// part_wave_bytes(RT) per wave); all but the last then count themselves
+// done in the second; the last waits for splits - 1 done, sets both
+// counters back to zero for the next call, and runs the epilogue on the sum
+// of all slots.  It only waits for workgroups that have already arrived (so
+// are running and wait for nothing), and the wait is bounded: counters that
+// do not start at zero give wrong results, never a hang.  Loads and stores
+// in ws_part are range-checked against part_bytes.
+//
+// Visibility across XCDs (each has its own L2) without fences: a fence at
+// device scope writes back and invalidates the whole L2 of the XCD, which
+// also throws away the operand tiles of every other workgroup there (the
+// first version, with fences and an acquiring spin, ran the vision
+// down-projection 1.5 to 2.7 times slower than without split-K).  Instead
+// the partial sums are stored and loaded with device scope (the SC1 cache
+// policy bit), which makes those accesses themselves coherent across the
+// device; every wave waits for its stores to complete (vmcnt(0)) before the
+// workgroup barrier that precedes the done count, and the counters are
+// relaxed device-scope atomics.
+constexpr int kScopeDevice = 16;      // cache policy SC1 (SC0 = 0): device scope
+constexpr uint32_t kPartQuad = 1024;  // one 16-byte quarter of an accumulator, all 64 lanes
+constexpr int kSpinLimit = 1 << 20;   // about 0.2 s of s_sleep 8
+__host__ __device__ constexpr uint32_t part_wave_bytes(int rt) { return 3u * 4u * kPartQuad * (uint32_t)rt; }
+
+template <int RT, bool kAcc, bool kBF, bool kSplit>
 __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                    int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
                                                    const uint32_t *__restrict__ centroids,
                                                    const uint16_t *__restrict__ scales, void *__restrict__ y,
-                                                   int32_t *__restrict__ acc_out, int nbm, int nbn, int f3d8) {
+                                                   int32_t *__restrict__ acc_out, int nbm, int nbn, int f3d8,
+                                                   int splits, int kbper, int32_t *__restrict__ ws_cnt,
+                                                   int32_t *__restrict__ ws_part, uint32_t part_bytes) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     constexpr int BM = 32 * RT;          // token rows per workgroup
     constexpr int NA = (2 * RT + 3) / 4;  // activation loads per wave and block
@@ -1629,10 +1672,17 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     const int tiles16 = (T + 15) >> 4;
     const uint32_t lane_off = (uint32_t)lane << 2;
 
-    int bm, bn;
-    if (!gemm_tile(nbm, nbn, bm, bn)) return;  // padding workgroup (grid rounded up to a multiple of 8)
+    // (the builds without split-K keep one range: they compile to the plain
+    // kernel, with no trace of the split-K code)
+    if constexpr (!kSplit) splits = 1;
+    int bm, bn, ks;
+    if (!gemm_tile(nbm, nbn, splits, bm, bn, ks)) return;  // padding workgroup (grid rounded up to a multiple of 8)
     const int row0 = bm * BM;
     const int frag0 = bn * kGemmBF + wave * 2;
+    // this workgroup's column blocks: kb0 .. kb0 + nkb - 1 (the host makes
+    // every range non-empty)
+    const int kb0 = kSplit ? ks * kbper : 0;
+    const int nkb = kSplit ? min(kbper, KB - kb0) : KB;
 
     // the table: S3D8's 96 bytes through the scalar cache; 3D8's 768 bytes as
     // one word per thread (an explicit load, waited for below; an
@@ -1681,13 +1731,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     uint32_t atail[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) atail[j] = acol[j] < ktail ? aoff[j] : kOOB;
-    // ND loads per wave and block, also for the blocks past the end, so that
-    // every wait below counts the same: those re-read the last block into a
-    // slot that is never read.  The per-lane offsets are block 0's; the
-    // block's byte offset goes in the scalar offset of the loads.
+    // ND loads per wave and block, also for the blocks past the end of the
+    // range, so that every wait below counts the same: those re-read the
+    // range's last block into a slot that is never read.  kb counts from the
+    // range's start.  The per-lane offsets are block 0's; the block's byte
+    // offset goes in the scalar offset of the loads.
     auto issue = [&](int kb, int slot) {
-        const int kbc = kb < KB ? kb : KB - 1;
-        const bool tail = kb >= KB - 1;
+        const int kbc = kb0 + (kb < nkb ? kb : nkb - 1);
+        const bool tail = kbc >= KB - 1;
         uint32_t lds[ND], vo[ND];
 #pragma unroll
         for (int j = 0; j < NA; ++j) {
@@ -1843,15 +1894,57 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 
     int kb = 0, slot = 0;
 #pragma unroll 1
-    for (; kb + 1 < KB; kb += 2) {
+    for (; kb + 1 < nkb; kb += 2) {
         block(a0, a1, b0, b1, kb, slot);
         slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
         block(a1, a0, b1, b0, kb + 1, slot);
         slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
     }
-    if (kb < KB) block(a0, a1, b0, b1, kb, slot);
+    if (kb < nkb) block(a0, a1, b0, b1, kb, slot);
     // loads of blocks past the end are still in flight: drain before exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    if (kSplit && splits > 1) {
+        // every workgroup of the tile stores its sums in slot `arrival`;
+        // the last then adds all slots (its own included, so that the
+        // accumulators are only ever read, as by the plain epilogue: adding
+        // into them here made the compiler move some out of the accumulator
+        // registers and spill inside the main loop)
+        __shared__ int arrival;
+        const int tile = bm * nbn + bn;
+        if (tid == 0)
+            arrival = __hip_atomic_fetch_add(ws_cnt + 2 * tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const int arr = min(max(arrival, 0), splits - 1);
+        const auto rp = make_rsrc(ws_part, part_bytes);
+        const uint32_t pb = ((uint32_t)(tile * splits + arr) * 4u + (uint32_t)wave) * part_wave_bytes(RT) + 16u * lane;
+#pragma unroll
+        for (int i = 0; i < RT; ++i)
+#pragma unroll
+            for (int d = 0; d < 3; ++d)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4i v{acc[i][d][4 * q], acc[i][d][4 * q + 1], acc[i][d][4 * q + 2], acc[i][d][4 * q + 3]};
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp,
+                                                           pb + (uint32_t)((i * 3 + d) * 4 + q) * kPartQuad, 0,
+                                                           kScopeDevice);
+                }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's sums are stored at device scope
+        __syncthreads();
+        if (arr < splits - 1) {
+            if (tid == 0) __hip_atomic_fetch_add(ws_cnt + 2 * tile + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (tid == 0) {
+            int spins = 0;
+            while (__hip_atomic_load(ws_cnt + 2 * tile + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < splits - 1 &&
+                   ++spins < kSpinLimit)
+                __builtin_amdgcn_s_sleep(8);
+            __hip_atomic_store(ws_cnt + 2 * tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws_cnt + 2 * tile + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+    }
 
     // epilogue: y = (xs[row] * acc) * alpha[ch] for channels 3 (16 frag0 +
     // c) + d, the three contiguous channels of lane c's triple
@@ -1865,7 +1958,51 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
         coff[d] = ok ? 4u * (uint32_t)(ch0 + d) : kOOB;
         sc[d] = bf16_to_f32(bload2(rsc, ok ? 2u * (uint32_t)(ch0 + d) : kOOB));
     }
-    store_tile_rows<true, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+    if (!kSplit || splits == 1) {
+        store_tile_rows<true, kAcc, RT, kBF>(acc, xs, M, N, row0, h, sc, coff, y, acc_out);
+        return;
+    }
+    // split-K, last workgroup of the tile: one 32-row tile at a time, the
+    // sum of all slots, two slots' loads (24 per lane) in flight at a time
+    // (the loads come from other XCDs' writes at device scope: one at a time
+    // they cost about half a microsecond each)
+    const auto rp = make_rsrc(ws_part, part_bytes);
+    const int tile = bm * nbn + bn;
+    const int rows = min(RT, (M - row0 + 31) / 32);
+#pragma unroll 1
+    for (int i = 0; i < rows; ++i) {
+        v16i sum[1][3] = {};
+#pragma unroll 1
+        for (int s = 0; s < splits; s += 2) {
+            uint4 v[2][12];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                // a missing second slot reads zeros (out-of-range offset)
+                const uint32_t pb =
+                    s + u < splits
+                        ? ((uint32_t)(tile * splits + s + u) * 4u + (uint32_t)wave) * part_wave_bytes(RT) + 16u * lane +
+                              (uint32_t)(12 * i) * kPartQuad
+                        : kOOB;
+#pragma unroll
+                for (int j = 0; j < 12; ++j)
+                    v[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                            rp, pb == kOOB ? kOOB : pb + (uint32_t)j * kPartQuad, 0,
+                                                            kScopeDevice));
+            }
+            __builtin_amdgcn_sched_barrier(0);  // all 24 loads issued before the first add waits
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int j = 0; j < 12; ++j) {
+                    const int d = j >> 2, q = j & 3;
+                    sum[0][d][4 * q] += (int32_t)v[u][j].x;
+                    sum[0][d][4 * q + 1] += (int32_t)v[u][j].y;
+                    sum[0][d][4 * q + 2] += (int32_t)v[u][j].z;
+                    sum[0][d][4 * q + 3] += (int32_t)v[u][j].w;
+                }
+        }
+        store_tile_rows<true, kAcc, 1, kBF>(sum, xs, M, N, row0 + 32 * i, h, sc, coff, y, acc_out);
+    }
 }
 
 // --------------------------------------------------------------- matrix-core rate probe
@@ -2527,6 +2664,93 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
 }
 
 namespace {
+// Launch plan of the fused GEMM (M > 16).
+//   rt      32-row tiles per wave (4 or 5): the height needing fewer
+//           workgroup rounds at one workgroup per CU, counted in units of
+//           row-tile work;
+//   splits  column-block ranges per tile (split-K), kbper blocks each;
+//   ws_cnt_bytes, ws_part_bytes: the split-K workspace (two counters per
+//           tile, padded to 256 bytes; `splits` partial-sum slots per tile).
+struct GemmPlan {
+    int rt, nbm, nbn, splits, kbper;
+    int64_t grid, ws_cnt_bytes, ws_part_bytes;
+};
+constexpr int kMaxSplits = 16;
+
+GemmPlan gemm_plan_rt(int64_t M, int64_t K, int64_t N, int rt, int splits) {
+    GemmPlan p{};
+    const int64_t T = (N + 2) / 3;
+    const int KB = (int)((K + 63) / 64);
+    p.rt = rt;
+    p.nbn = (int)(((T + 15) / 16 + kGemmBF - 1) / kGemmBF);
+    p.nbm = (int)((M + 32 * rt - 1) / (32 * rt));
+    const int s = splits < 1 ? 1 : splits > KB ? KB : splits;
+    p.kbper = (KB + s - 1) / s;
+    p.splits = (KB + p.kbper - 1) / p.kbper;  // every range non-empty
+    const int64_t tiles = (int64_t)p.nbm * p.nbn;
+    p.grid = (tiles * p.splits + kXcds - 1) / kXcds * kXcds;
+    p.ws_cnt_bytes = p.splits > 1 ? (2 * 4 * tiles + 255) / 256 * 256 : 0;
+    p.ws_part_bytes = p.splits > 1 ? tiles * p.splits * 4 * (int64_t)part_wave_bytes(rt) : 0;
+    return p;
+}
+
+int gemm_rt(int64_t M, int64_t N, int cus) {
+    const int64_t T = (N + 2) / 3;
+    const int64_t nbn = ((T + 15) / 16 + kGemmBF - 1) / kGemmBF;
+    auto cost = [&](int rt) {
+        const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
+        return (tiles + cus - 1) / cus * rt;
+    };
+    return cost(5) < cost(4) ? 5 : 4;
+}
+
+// The automatic split count.  A split into S ranges runs ceil(KB/S) blocks
+// per workgroup and then a fixup whose cost grows with S: the last
+// workgroup of a tile reads all S slots of partial sums.  Measured on the
+// vision down-projection (80 blocks, 52 tiles of 128 rows): each slot costs
+// about as much as 9 column blocks of the main loop (44.0 / 42.3 / 46.5 us
+// at S = 2 / 3 / 4, against 57.1 us unsplit), so S minimises
+// ceil(KB/S) + 9 S over the counts whose workgroups fit one round on the
+// CUs (tiles x S <= CUs), at most 16.
+constexpr int kSplitSlotBlocks = 9;
+int gemm_auto_splits(int64_t M, int64_t K, int64_t N, int cus) {
+    if (M <= 16) return 1;
+    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), 1);
+    const int64_t tiles = (int64_t)p.nbm * p.nbn;
+    const int64_t KB = (K + 63) / 64;
+    int best = 1;
+    int64_t best_cost = KB + kSplitSlotBlocks;
+    for (int64_t s = 2; s <= kMaxSplits && s <= KB && tiles * s <= cus; ++s) {
+        const int64_t cost = (KB + s - 1) / s + kSplitSlotBlocks * s;
+        if (cost < best_cost) best = (int)s, best_cost = cost;
+    }
+    return best;
+}
+
+typedef void (*GemmFn)(const int8_t *, const float *, int, int, int, int, const uint8_t *, const uint32_t *,
+                       const uint16_t *, void *, int32_t *, int, int, int, int, int, int32_t *, int32_t *, uint32_t);
+
+// Enqueue the fused GEMM under plan p (workspace checked by the caller).
+int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
+                const uint8_t *tiled, const uint32_t *table32, bool f3d8, const uint16_t *scales_bf16, void *y,
+                bool obf, int32_t *acc_out, void *ws, hipStream_t stream) {
+    if (p.grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
+#define S3D8_GEMM_BUILDS(sk)                                                               \
+    {{{gemm_kernel<4, false, false, sk>, gemm_kernel<4, false, true, sk>},                 \
+      {gemm_kernel<4, true, false, sk>, gemm_kernel<4, true, true, sk>}},                  \
+     {{gemm_kernel<5, false, false, sk>, gemm_kernel<5, false, true, sk>},                 \
+      {gemm_kernel<5, true, false, sk>, gemm_kernel<5, true, true, sk>}}}
+    static const GemmFn fns[2][2][2][2] = {S3D8_GEMM_BUILDS(false), S3D8_GEMM_BUILDS(true)};
+#undef S3D8_GEMM_BUILDS
+    const bool split = p.splits > 1;
+    int32_t *cnt = split ? static_cast<int32_t *>(ws) : nullptr;
+    int32_t *part = split ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.ws_cnt_bytes) : nullptr;
+    hipLaunchKernelGGL(fns[split][p.rt == 5][acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(256), 0, stream,
+                       xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled, table32, scales_bf16, y, acc_out,
+                       p.nbm, p.nbn, (int)f3d8, p.splits, p.kbper, cnt, part, (uint32_t)p.ws_part_bytes);
+    return launch_status();
+}
+
 int check_linear_args(const void *tiled, int64_t tiled_size, const void *table, const uint16_t *scales,
                       const void *y, int64_t M, int64_t K, int64_t N) {
     if (!tiled || !table || !scales || !y) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
@@ -2564,30 +2788,9 @@ int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
     const uint32_t *table32 = reinterpret_cast<const uint32_t *>(table);
     if (M > 16) {
         if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
-        const int64_t T = (N + 2) / 3;
-        const int nbn = (int)(((T + 15) / 16 + kGemmBF - 1) / kGemmBF);
-        // 4 or 5 row tiles per wave: the one that needs fewer workgroup
-        // rounds (one workgroup per CU), counted in units of row-tile work
-        auto cost = [&](int rt) {
-            const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
-            return (tiles + cus - 1) / cus * rt;
-        };
-        const int rt = cost(5) < cost(4) ? 5 : 4;
-        const int nbm = (int)((M + 32 * rt - 1) / (32 * rt));
-        const int64_t nwg = (int64_t)nbm * nbn;
-        const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
-        if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-        typedef void (*GemmFn)(const int8_t *, const float *, int, int, int, int, const uint8_t *, const uint32_t *,
-                               const uint16_t *, void *, int32_t *, int, int, int);
-        static const GemmFn fns[2][2][2] = {
-            {{gemm_kernel<4, false, false>, gemm_kernel<4, false, true>},
-             {gemm_kernel<4, true, false>, gemm_kernel<4, true, true>}},
-            {{gemm_kernel<5, false, false>, gemm_kernel<5, false, true>},
-             {gemm_kernel<5, true, false>, gemm_kernel<5, true, true>}}};
-        hipLaunchKernelGGL(fns[rt == 5][acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0,
-                           (hipStream_t)stream, xq, xs, (int)M, (int)K, (int)N, (int)T, tiled, table32, scales_bf16, y,
-                           acc_out, nbm, nbn, (int)f3d8);
-        return launch_status();
+        const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), 1);
+        return launch_gemm(p, xq, xs, M, K, N, tiled, table32, f3d8, scales_bf16, y, obf, acc_out, nullptr,
+                           (hipStream_t)stream);
     }
     // up to 8 token rows: the streaming GEMV on the codes, when they fit it
     if (launch_gemv_codes(xq, xs, M, K, N, tiled, table, f3d8, scales_bf16, y, obf, acc_out, cus,
@@ -2604,6 +2807,43 @@ int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
             return s3d8::fail(S3D8_ERR_INVALID_ARG, "no GEMV variant for this launch shape");
     }
     return launch_status();
+}
+
+int splitk_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                int64_t tiled_size, const void *table, bool f3d8, const uint16_t *scales_bf16, void *y, bool obf,
+                int32_t *acc_out, int32_t splits, void *ws, int64_t ws_bytes, void *stream) {
+    if (splits < 0) return s3d8::fail(S3D8_ERR_INVALID_ARG, "splits must be 0 (automatic) or positive");
+    if (M <= 16)  // the GEMV paths: no split, no workspace
+        return linear_impl(xq, xs, M, K, N, tiled, tiled_size, table, f3d8, scales_bf16, y, obf, acc_out, stream);
+    if (!xq || !xs) return s3d8::fail(S3D8_ERR_INVALID_ARG, "null pointer argument");
+    int rc = check_linear_args(tiled, tiled_size, table, scales_bf16, y, M, K, N);
+    if (rc) return rc;
+    if (!aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "xq must be 16-byte aligned");
+    if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
+    // the workspace against the documented size (the larger of the two tile
+    // heights' needs), checked before the device for an explicit count
+    auto check_ws = [&](int s) {
+        const int64_t need = s3d8_splitk_workspace_bytes(M, K, N, s);
+        if (need == 0) return (int)S3D8_OK;
+        for (int rt = 4; rt <= 5; ++rt)
+            if (gemm_plan_rt(M, K, N, rt, s).ws_part_bytes > 2147483647)
+                return s3d8::fail(S3D8_ERR_SHAPE, "split-K partial sums over 2^31 bytes: use fewer splits");
+        if (!ws) return s3d8::fail(S3D8_ERR_INVALID_ARG, "split-K needs a workspace");
+        if (ws_bytes < need)
+            return s3d8::fail(S3D8_ERR_INVALID_ARG, "workspace below s3d8_splitk_workspace_bytes(M, K, N, splits)");
+        if (reinterpret_cast<uintptr_t>(ws) & 255u)
+            return s3d8::fail(S3D8_ERR_ALIGN, "the split-K workspace must be 256-byte aligned");
+        return (int)S3D8_OK;
+    };
+    if (splits > 0 && (rc = check_ws(splits))) return rc;
+    int cus = 0;
+    rc = check_device(&cus);
+    if (rc) return rc;
+    const int s = splits == 0 ? gemm_auto_splits(M, K, N, cus) : splits;
+    if (splits == 0 && (rc = check_ws(s))) return rc;
+    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), s);
+    return launch_gemm(p, xq, xs, M, K, N, tiled, reinterpret_cast<const uint32_t *>(table), f3d8, scales_bf16, y, obf,
+                       acc_out, ws, (hipStream_t)stream);
 }
 
 int forward_impl(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_size,
@@ -2647,6 +2887,32 @@ int32_t s3d8_linear_ex(const int8_t *xq, const float *xs, int64_t M, int64_t K, 
     if (rc) return rc;
     return linear_impl(xq, xs, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
                        out_type == S3D8_OUT_BF16, acc_out, stream);
+}
+
+int32_t s3d8_splitk_auto(int64_t M, int64_t K, int64_t N, int32_t num_cus) {
+    if (M <= 0 || K <= 0 || N <= 0 || num_cus < 1) return -1;
+    return gemm_auto_splits(M, K, N, num_cus);
+}
+
+int64_t s3d8_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t splits) {
+    if (M <= 0 || K <= 0 || N <= 0 || splits < 1) return -1;
+    if (M <= 16) return 0;
+    int64_t most = 0;
+    for (int rt = 4; rt <= 5; ++rt) {
+        const GemmPlan p = gemm_plan_rt(M, K, N, rt, splits);
+        most = std::max(most, p.ws_cnt_bytes + p.ws_part_bytes);
+    }
+    return most;
+}
+
+int32_t s3d8_linear_splitk(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N, const uint8_t *tiled,
+                           int64_t tiled_bytes, const void *table, int32_t format, const uint16_t *scales_bf16,
+                           void *y, int32_t out_type, int32_t *acc_out, int32_t splits, void *workspace,
+                           int64_t workspace_bytes, void *stream) {
+    int rc = check_variant(format, out_type);
+    if (rc) return rc;
+    return splitk_impl(xq, xs, M, K, N, tiled, tiled_bytes, table, format == S3D8_FORMAT_3D8, scales_bf16, y,
+                       out_type == S3D8_OUT_BF16, acc_out, splits, workspace, workspace_bytes, stream);
 }
 
 int32_t s3d8_forward(const float *x, int64_t M, int64_t K, int64_t N, const uint8_t *tiled, int64_t tiled_bytes,
