@@ -352,7 +352,8 @@ def test_variant_entry_points_validation():
 def _splitk_bytes_closed_form(M, K, N, splits):
     """Two int32 counters per output tile (padded to 256 bytes) plus, per
     tile, `splits` slots of 4 waves x 3 RT accumulators x 64 lanes x 16
-    int32; the larger need of the two tile heights (RT = 4, 5 rows of 32)."""
+    int32; the largest need of the three tile heights (RT = 2, 4, 5 rows of
+    32)."""
     T = -(-N // 3)
     KB = -(-K // 64)
     s = max(1, min(splits, KB))
@@ -361,7 +362,7 @@ def _splitk_bytes_closed_form(M, K, N, splits):
     if M <= 16 or s == 1:
         return 0
     best = 0
-    for rt in (4, 5):
+    for rt in (2, 4, 5):
         tiles = -(-M // (32 * rt)) * -(-(-(-T // 16)) // 8)
         best = max(best, -(-(8 * tiles) // 256) * 256 + tiles * s * 4 * 3 * rt * 64 * 16 * 4)
     return best
@@ -377,13 +378,15 @@ def test_splitk_workspace_bytes(M, K, N, splits):
 
 def test_splitk_sizes_and_choice():
     L = _lib.lib()
-    # worked case: the vision MLP down-projection at 1601 tokens needs 13 x 4
-    # tiles of 128 rows x 384 channels (52 of 256 CUs) and has 80 column
-    # blocks: ceil(80/S) + 9 S is 89, 58, 54, 56 for S = 1..4, so 3 ranges;
-    # its workspace at 4 (RT = 5 is the larger: 11 x 4 tiles)
-    assert L.s3d8_splitk_auto(1601, 5120, 1280, 256) == 3
+    # worked case: the vision MLP down-projection at 1601 tokens takes
+    # 64-row tiles (26 x 4 = 104 tiles of 64 rows x 384 channels, one round
+    # on 256 CUs, against 52 tiles of 128 rows) and has 80 column blocks:
+    # ceil(80/S) + 9 S is 89, 58 for S = 1, 2 and 3 x 104 tiles would not fit
+    # one round, so 2 ranges; its workspace at 4 (RT = 5 needs the most:
+    # 11 x 4 tiles)
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 256) == 2
     assert L.s3d8_splitk_workspace_bytes(1601, 5120, 1280, 4) == 512 + 44 * 4 * 4 * 61440
-    assert L.s3d8_splitk_auto(1601, 5120, 1280, 104) == 2  # 3 x 52 tiles would not fit one round
+    assert L.s3d8_splitk_auto(1601, 5120, 1280, 104) == 1  # 104 tiles fill every CU
     assert L.s3d8_splitk_auto(1601, 5120, 1280, 103) == 1
     assert L.s3d8_splitk_auto(1601, 1280, 5120, 256) == 1  # up-projection: 182 tiles
     assert L.s3d8_splitk_auto(2048, 4096, 14336, 256) == 1

@@ -123,19 +123,21 @@ def test_prefill_full_output_matches_oracle(gpu, name, path, mode):
 
 
 # ------------------------------------------------------------------ ragged shapes, every mode
-# (M, K, N): row tails of both row-tile heights (1270 and 2000 take 160-row
-# tiles, 300 and 33 take 128-row tiles), ragged triples (N mod 3 = 1, 2),
-# K past the last 64-column block, and small M through the GEMV kernels.
-RAGGED = [(1270, 80, 12280), (2000, 1024, 14335), (300, 1040, 772), (33, 1040, 97), (17, 80, 50),
-          (16, 1040, 97), (9, 256, 48), (5, 64, 47), (1, 4096, 300)]
+# (M, K, N): row tails of every row-tile height (1270 and 2000 take
+# 160-row tiles, 600 takes 128-row tiles, 300, 33 and 17 take 64-row tiles),
+# ragged triples (N mod 3 = 1, 2), K past the last 64-column block, and
+# small M through the GEMV kernels.
+RAGGED = [(1270, 80, 12280), (2000, 1024, 14335), (600, 80, 12280), (300, 1040, 772), (33, 1040, 97),
+          (17, 80, 50), (16, 1040, 97), (9, 256, 48), (5, 64, 47), (1, 4096, 300)]
 
 
 @pytest.mark.parametrize("name,splits", [("vision_down", 2), ("vision_down", 3), ("vision_down", 5),
                                          ("vision_up", 2), ("vision_up", 4), ("c3", 2)])
 def test_splitk_full_output_matches_oracle(gpu, name, splits):
     """Split-K at the full prefill sizes with explicit split counts (vision
-    down: 80 blocks in 2, 3 or 5 ranges; vision up: 20 blocks; c3 on
-    160-row tiles), accumulators and fp32 outputs in full."""
+    down on 64-row tiles: 80 blocks in 2, 3 or 5 ranges; vision up on 128-row
+    tiles: 20 blocks; c3 on 160-row tiles), accumulators and fp32 outputs in
+    full."""
     lin = PREFILL[name]
     x, C, alpha, packed, xq_r, xs_r, acc_r, y_r = _oracle_full(name)
     got = _run_prefill(gpu, "splitk%d" % splits, "acc", x, C, alpha, packed, lin.N)
@@ -188,11 +190,11 @@ def test_forward_modes(gpu, M, K, N, mode):
 
 # K = 1040: 17 column blocks, the last one ragged (16 columns)
 @pytest.mark.parametrize("splits", [2, 3, 4, 5, 7, 16, 17, 40])
-@pytest.mark.parametrize("M,N", [(300, 772), (1270, 97), (33, 12280)])
+@pytest.mark.parametrize("M,N", [(300, 772), (600, 12280), (33, 12280)])
 def test_splitk_split_counts(gpu, M, N, splits):
     """Every split count on a ragged K: unequal ranges, one block per range
-    (17), more ranges requested than blocks (40 is clamped to 17), both
-    row-tile heights."""
+    (17), more ranges requested than blocks (40 is clamped to 17), on 64-row
+    (300 x 772, 33 x 12280) and 128-row tiles (600 x 12280)."""
     K = 1040
     C, alpha, packed = random_format([4020, M, K, N], N, K)
     x = workloads.gaussian_matrix([4021, M, K], M, K)

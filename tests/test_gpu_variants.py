@@ -5,7 +5,7 @@ whole byte indexes a (256, 3) table of signed values) and bfloat16 outputs
 (blog "Fused matrix-vector product": results are converted to bf16 on the way
 out), through every kernel path: the streaming GEMV (M <= 4), the fused GEMV
 fallback, the GEMV on pre-quantised activations (M <= 16), the fused GEMM
-(both row-tile variants, whole and split-K), the unfused decode + INT8 GEMM
+(all three row-tile heights, whole and split-K), the unfused decode + INT8 GEMM
 and the standalone dequantisation.
 
 Bar: codes, scales, decoded weights and INT32 accumulators bit-exact; fp32
@@ -112,14 +112,16 @@ def test_dequant_3d8_every_byte_value(gpu):
 # (kind, M, K, N): forward at M <= 4 is the streaming GEMV; at N = 200000
 # (over 16 tiles per CU) the fused GEMV; M = 4 with K = 5120 and M = 8 run
 # quantisation then the GEMV on quantised activations (as linear at M <= 16);
-# M = 40 / 300 the fused GEMM (row tiles of 128 and 160), also split into 3
-# column-block ranges (split-K).
+# the fused GEMM on 64-row tiles (M = 40, 300), 128-row tiles (M = 600) and
+# 160-row tiles (M = 1270), also split into 3 column-block ranges (split-K;
+# K = 80 has 2 blocks, so 2 ranges).
 PATHS = [
     ("forward", 1, 256, 384), ("forward", 2, 1040, 97), ("forward", 3, 4096, 50), ("forward", 4, 64, 47),
     ("forward", 1, 64, 200000), ("forward", 4, 5120, 101), ("forward", 8, 1280, 98), ("linear", 1, 80, 50),
     ("linear", 16, 1040, 97),
-    ("linear", 40, 256, 385), ("linear", 300, 1040, 772), ("unfused", 40, 1040, 97), ("unfused", 129, 256, 385),
-    ("splitk", 40, 1040, 97), ("splitk", 300, 1040, 772),
+    ("linear", 40, 256, 385), ("linear", 300, 1040, 772), ("linear", 600, 80, 12280), ("linear", 1270, 80, 12280),
+    ("unfused", 40, 1040, 97), ("unfused", 129, 256, 385),
+    ("splitk", 40, 1040, 97), ("splitk", 300, 1040, 772), ("splitk", 600, 1040, 12280), ("splitk", 1270, 80, 12280),
 ]
 
 

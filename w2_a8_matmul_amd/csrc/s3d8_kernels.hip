@@ -163,8 +163,19 @@ template <int NA>
 __device__ __forceinline__ void load_block_to_lds(const uint32_t (&lds)[NA + 2], const uint32_t (&voff)[NA + 2],
                                                   v4i ra, uint32_t sa, v4i rw, uint32_t sw) {
     uint32_t saved;
-    static_assert(NA == 2 || NA == 3, "two or three activation loads per block");
-    if constexpr (NA == 3) {
+    static_assert(NA >= 1 && NA <= 3, "one to three activation loads per block");
+    if constexpr (NA == 1) {
+        asm volatile(
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %4, %7, %8 offen lds\n\t"
+            "s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %5, %9, %10 offen lds\n\t"
+            "s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %9, %10 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
+            : "s"(lds[0]), "s"(lds[1]), "s"(lds[2]), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "s"(ra), "s"(sa),
+              "s"(rw), "s"(sw)
+            : "memory");
+    } else if constexpr (NA == 3) {
         asm volatile(
             "s_mov_b32 %0, m0\n\t"
             "s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %6, %11, %12 offen lds\n\t"
@@ -1425,9 +1436,9 @@ __global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restri
 // on v_mfma_i32_32x32x32_i8 (INT32 accumulation).
 //
 // Workgroup tile = 32 RT token rows x 128 channel triples (384 output
-// channels), RT = 4 or 5; 4 waves side by side along N, each 32 RT rows x
+// channels), RT = 2, 4 or 5; 4 waves side by side along N, each 32 RT rows x
 // 32 triples = RT row tiles x 3 channels of the triple = 3 RT accumulators
-// of 32 x 32 (192 or 240 AGPRs, one wave per SIMD).  Per 64-column block of K:
+// of 32 x 32 (96, 192 or 240 AGPRs, one wave per SIMD).  Per 64-column block of K:
 //  - activations (32 RT x 64 INT8) and the packed weights (128 triples x 64)
 //    are copied straight from memory into LDS by buffer loads with the LDS
 //    destination bit (no registers involved), four blocks ahead of use, into
@@ -1490,15 +1501,17 @@ __device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
 // the same followed by lgkmcnt(0) and a workgroup barrier.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N == 8 || N == 10 || N == 12 || N == 15, "add the immediate");
+    static_assert(N == 8 || N == 9 || N == 10 || N == 12 || N == 15, "add the immediate");
     if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     if constexpr (N == 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
-    static_assert(N == 8 || N == 10, "add the immediate");
+    static_assert(N == 6 || N == 8 || N == 10, "add the immediate");
+    if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -1848,12 +1861,16 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // 2 (g - TR0) + 1.  At RT = 5 (ten groups) LK0 = 2 and TR0 = 6: the raw
     // weights have two groups of MFMAs to land behind and every lookup four
     // (measured at c3 about 2.5 % faster than LK0 = 1, TR0 = 3, which is all
-    // that the eight groups at RT = 4 leave room for).
+    // that the eight groups at RT = 4 leave room for).  RT = 2 (64-row tiles,
+    // for shapes with few output tiles) has four groups: the lookups of
+    // dwords 0..3 in group 1 and of 4..7 in group 2, their transposes one
+    // group later.
     // Inside a group
     // each MFMA is followed by a share of the VALU and LDS work, since one
     // wave per SIMD only overlaps what lies between its MFMAs; sched_barrier
     // keeps the compiler from regrouping across groups.
-    static_assert(2 * RT >= 7, "the block schedule needs seven groups");
+    static_assert(RT == 2 || 2 * RT >= 7, "the block schedule needs seven groups, or the four of RT = 2");
+    constexpr int kGrpValu = RT == 2 ? 8 : 6, kGrpLds = RT == 2 ? 6 : 4;
     auto block = [&](const v4i (&ac)[RT][2], v4i (&an)[RT][2], const v4i (&bc)[2][3], v4i (&bnx)[2][3], int kb,
                      int slot) {
         wait_vmcnt_barrier<2 * ND>();
@@ -1872,21 +1889,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 #pragma unroll
             for (int r = 0; r < RT; ++r)
                 if (g == r % 4) read_a(an, next, r);
-            constexpr int LK0 = RT == 5 ? 2 : 1;
-            if (g >= LK0 && g <= LK0 + 3) {
-                lookups(wn, 2 * (g - LK0), q[2 * (g - LK0)]);
-                lookups(wn, 2 * (g - LK0) + 1, q[2 * (g - LK0) + 1]);
-            }
-            constexpr int TR0 = RT == 5 ? 6 : 3;
-            if (g >= TR0 && g <= TR0 + 3) {
-                transpose(q[2 * (g - TR0)], bnx, 2 * (g - TR0));
-                transpose(q[2 * (g - TR0) + 1], bnx, 2 * (g - TR0) + 1);
+            if constexpr (RT == 2) {
+                if (g == 1 || g == 2)
+#pragma unroll
+                    for (int p = 4 * (g - 1); p < 4 * g; ++p) lookups(wn, p, q[p]);
+                if (g == 2 || g == 3)
+#pragma unroll
+                    for (int p = 4 * (g - 2); p < 4 * (g - 1); ++p) transpose(q[p], bnx, p);
+            } else {
+                constexpr int LK0 = RT == 5 ? 2 : 1;
+                if (g >= LK0 && g <= LK0 + 3) {
+                    lookups(wn, 2 * (g - LK0), q[2 * (g - LK0)]);
+                    lookups(wn, 2 * (g - LK0) + 1, q[2 * (g - LK0) + 1]);
+                }
+                constexpr int TR0 = RT == 5 ? 6 : 3;
+                if (g >= TR0 && g <= TR0 + 3) {
+                    transpose(q[2 * (g - TR0)], bnx, 2 * (g - TR0));
+                    transpose(q[2 * (g - TR0) + 1], bnx, 2 * (g - TR0) + 1);
+                }
             }
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // up to six VALU
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // up to four LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, kGrpValu, 0);  // a share of the VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, kGrpLds, 0);   // and of the LDS reads
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -2665,9 +2691,7 @@ int32_t s3d8_tile(const uint8_t *packed, int64_t N, int64_t K, uint8_t *tiled, v
 
 namespace {
 // Launch plan of the fused GEMM (M > 16).
-//   rt      32-row tiles per wave (4 or 5): the height needing fewer
-//           workgroup rounds at one workgroup per CU, counted in units of
-//           row-tile work;
+//   rt      32-row tiles per wave (2, 4 or 5, gemm_rt);
 //   splits  column-block ranges per tile (split-K), kbper blocks each;
 //   ws_cnt_bytes, ws_part_bytes: the split-K workspace (two counters per
 //           tile, padded to 256 bytes; `splits` partial-sum slots per tile).
@@ -2676,6 +2700,7 @@ struct GemmPlan {
     int64_t grid, ws_cnt_bytes, ws_part_bytes;
 };
 constexpr int kMaxSplits = 16;
+constexpr int64_t kClkBlockRT2 = 1250;  // clocks per 64-column block at 64-row tiles (measured)
 
 GemmPlan gemm_plan_rt(int64_t M, int64_t K, int64_t N, int rt, int splits) {
     GemmPlan p{};
@@ -2694,14 +2719,23 @@ GemmPlan gemm_plan_rt(int64_t M, int64_t K, int64_t N, int rt, int splits) {
     return p;
 }
 
-int gemm_rt(int64_t M, int64_t N, int cus) {
+// Tile height: 2, 4 or 5 row tiles of 32 per wave, the one with the least
+// estimated time at one workgroup per CU: workgroup rounds x (64-column
+// blocks x clocks per block + a fixed prologue and epilogue), with the
+// clocks measured on this part.  Taller tiles reuse each decoded weight
+// over more rows; shorter ones make more workgroups, which pays when the
+// taller tiles leave CUs idle (the vision down-projection: 52 tiles of 128
+// rows, 104 of 64).
+int gemm_rt(int64_t M, int64_t K, int64_t N, int cus) {
     const int64_t T = (N + 2) / 3;
     const int64_t nbn = ((T + 15) / 16 + kGemmBF - 1) / kGemmBF;
-    auto cost = [&](int rt) {
+    const int64_t KB = (K + 63) / 64;
+    auto cost = [&](int rt, int64_t clk_block, int64_t clk_fixed) {
         const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
-        return (tiles + cus - 1) / cus * rt;
+        return (tiles + cus - 1) / cus * (KB * clk_block + clk_fixed);
     };
-    return cost(5) < cost(4) ? 5 : 4;
+    const int64_t c2 = cost(2, kClkBlockRT2, 18000), c4 = cost(4, 1400, 26000), c5 = cost(5, 1663, 30000);
+    return c5 < c4 && c5 < c2 ? 5 : c2 < c4 ? 2 : 4;
 }
 
 // The automatic split count.  A split into S ranges runs ceil(KB/S) blocks
@@ -2715,7 +2749,7 @@ int gemm_rt(int64_t M, int64_t N, int cus) {
 constexpr int kSplitSlotBlocks = 9;
 int gemm_auto_splits(int64_t M, int64_t K, int64_t N, int cus) {
     if (M <= 16) return 1;
-    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), 1);
+    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, K, N, cus), 1);
     const int64_t tiles = (int64_t)p.nbm * p.nbn;
     const int64_t KB = (K + 63) / 64;
     int best = 1;
@@ -2735,17 +2769,18 @@ int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M,
                 const uint8_t *tiled, const uint32_t *table32, bool f3d8, const uint16_t *scales_bf16, void *y,
                 bool obf, int32_t *acc_out, void *ws, hipStream_t stream) {
     if (p.grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-#define S3D8_GEMM_BUILDS(sk)                                                               \
-    {{{gemm_kernel<4, false, false, sk>, gemm_kernel<4, false, true, sk>},                 \
-      {gemm_kernel<4, true, false, sk>, gemm_kernel<4, true, true, sk>}},                  \
-     {{gemm_kernel<5, false, false, sk>, gemm_kernel<5, false, true, sk>},                 \
-      {gemm_kernel<5, true, false, sk>, gemm_kernel<5, true, true, sk>}}}
-    static const GemmFn fns[2][2][2][2] = {S3D8_GEMM_BUILDS(false), S3D8_GEMM_BUILDS(true)};
+#define S3D8_GEMM_RT(rt, sk)                                                         \
+    {{gemm_kernel<rt, false, false, sk>, gemm_kernel<rt, false, true, sk>},          \
+     {gemm_kernel<rt, true, false, sk>, gemm_kernel<rt, true, true, sk>}}
+#define S3D8_GEMM_BUILDS(sk) {S3D8_GEMM_RT(2, sk), S3D8_GEMM_RT(4, sk), S3D8_GEMM_RT(5, sk)}
+    static const GemmFn fns[2][3][2][2] = {S3D8_GEMM_BUILDS(false), S3D8_GEMM_BUILDS(true)};
 #undef S3D8_GEMM_BUILDS
+#undef S3D8_GEMM_RT
     const bool split = p.splits > 1;
     int32_t *cnt = split ? static_cast<int32_t *>(ws) : nullptr;
     int32_t *part = split ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.ws_cnt_bytes) : nullptr;
-    hipLaunchKernelGGL(fns[split][p.rt == 5][acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(fns[split][p.rt == 2 ? 0 : p.rt == 4 ? 1 : 2][acc_out != nullptr][obf], dim3((unsigned)p.grid),
+                       dim3(256), 0, stream,
                        xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled, table32, scales_bf16, y, acc_out,
                        p.nbm, p.nbn, (int)f3d8, p.splits, p.kbper, cnt, part, (uint32_t)p.ws_part_bytes);
     return launch_status();
@@ -2788,7 +2823,7 @@ int linear_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
     const uint32_t *table32 = reinterpret_cast<const uint32_t *>(table);
     if (M > 16) {
         if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
-        const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), 1);
+        const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, K, N, cus), 1);
         return launch_gemm(p, xq, xs, M, K, N, tiled, table32, f3d8, scales_bf16, y, obf, acc_out, nullptr,
                            (hipStream_t)stream);
     }
@@ -2820,12 +2855,12 @@ int splitk_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
     if (rc) return rc;
     if (!aligned16(xq)) return s3d8::fail(S3D8_ERR_ALIGN, "xq must be 16-byte aligned");
     if (N > kGemmMaxN) return s3d8::fail(S3D8_ERR_SHAPE, "N over 3355442 is not supported for M > 16");
-    // the workspace against the documented size (the larger of the two tile
-    // heights' needs), checked before the device for an explicit count
+    // the workspace against the documented size (the largest of the three
+    // tile heights' needs), checked before the device for an explicit count
     auto check_ws = [&](int s) {
         const int64_t need = s3d8_splitk_workspace_bytes(M, K, N, s);
         if (need == 0) return (int)S3D8_OK;
-        for (int rt = 4; rt <= 5; ++rt)
+        for (int rt : {2, 4, 5})
             if (gemm_plan_rt(M, K, N, rt, s).ws_part_bytes > 2147483647)
                 return s3d8::fail(S3D8_ERR_SHAPE, "split-K partial sums over 2^31 bytes: use fewer splits");
         if (!ws) return s3d8::fail(S3D8_ERR_INVALID_ARG, "split-K needs a workspace");
@@ -2841,7 +2876,7 @@ int splitk_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t
     if (rc) return rc;
     const int s = splits == 0 ? gemm_auto_splits(M, K, N, cus) : splits;
     if (splits == 0 && (rc = check_ws(s))) return rc;
-    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, N, cus), s);
+    const GemmPlan p = gemm_plan_rt(M, K, N, gemm_rt(M, K, N, cus), s);
     return launch_gemm(p, xq, xs, M, K, N, tiled, reinterpret_cast<const uint32_t *>(table), f3d8, scales_bf16, y, obf,
                        acc_out, ws, (hipStream_t)stream);
 }
@@ -2898,7 +2933,7 @@ int64_t s3d8_splitk_workspace_bytes(int64_t M, int64_t K, int64_t N, int32_t spl
     if (M <= 0 || K <= 0 || N <= 0 || splits < 1) return -1;
     if (M <= 16) return 0;
     int64_t most = 0;
-    for (int rt = 4; rt <= 5; ++rt) {
+    for (int rt : {2, 4, 5}) {
         const GemmPlan p = gemm_plan_rt(M, K, N, rt, splits);
         most = std::max(most, p.ws_cnt_bytes + p.ws_part_bytes);
     }
