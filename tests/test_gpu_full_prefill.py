@@ -235,3 +235,44 @@ def test_splitk_small_m_takes_gemv(gpu):
     assert s3d8.splitk_workspace_bytes(M, K, N, 4) == 0
     got = _run_prefill(gpu, "splitk4", "acc", x, C, alpha, packed, N)
     _compare(got, xq_r, xs_r, acc_r, y_r, "acc")
+
+
+def test_splitk_graph_replays(gpu):
+    """s3d8_linear_splitk captured in a HIP graph (as the benchmark times it):
+    every replay, with eager calls on the same workspace in between, gives the
+    oracle's results, and the workspace counters are back at zero after each
+    (the counters are reset by the kernels themselves, no memset node)."""
+    M, K, N, splits = 300, 5120, 1280, 4
+    C, alpha, packed = random_format([4050], N, K)
+    x = workloads.gaussian_matrix([4051], M, K)
+    _, _, acc_r, y_r = oracle.linear(x, packed, C, alpha, N)
+    xq, xs = s3d8.quant_act(dev(x, gpu))
+    tiled = s3d8.tile(dev(packed, gpu), N)
+    Cd, Sd = dev(C, gpu), dev(alpha.view(np.int16), gpu)
+    ws = torch.zeros((s3d8.splitk_workspace_bytes(M, K, N, splits),), dtype=torch.uint8, device=gpu)
+    y = torch.empty((M, N), dtype=torch.float32, device=gpu)
+    acc = torch.empty((M, N), dtype=torch.int32, device=gpu)
+
+    def call():
+        s3d8.linear_splitk(xq, xs, tiled, Cd, Sd, N, splits=splits, workspace=ws, y=y, acc=acc, return_acc=True)
+
+    call()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream(device=gpu)
+    s.wait_stream(torch.cuda.current_stream(gpu))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        y.zero_()
+        acc.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
+        check_y(y.cpu().numpy(), y_r)
+        assert int(ws[:256].count_nonzero()) == 0
+        # eager work on the same workspace between replays
+        call()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc.cpu().numpy(), acc_r)
