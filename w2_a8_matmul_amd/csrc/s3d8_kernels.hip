@@ -3091,8 +3091,8 @@ int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_
                        tiled, reinterpret_cast<const uint32_t *>(table), (int)K, (int)T, KB, nchunks, workspace,
                        (int)f3d8);
     const int nbn = (int)((3 * T + 383) / 384);
-    // 4 or 5 row tiles per wave, as for the fused GEMM: the one that needs
-    // fewer workgroup rounds, counted in units of row-tile work
+    // 4 or 5 row tiles per wave: the one that needs fewer workgroup rounds,
+    // counted in units of row-tile work (this kernel has no 64-row build)
     auto cost = [&](int rt) {
         const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
         return (tiles + cus - 1) / cus * rt;
