@@ -380,7 +380,10 @@ int32_t s3d8_linear_splitk(const int8_t *xq, const float *xs, int64_t M, int64_t
  * (the main loop's 64-column blocks per workgroup plus the measured cost of
  * adding S slots of partial sums, in the same unit) among 1 and the counts
  * whose workgroups fit one round on the CUs (output tiles x S <= num_cus),
- * at most 16.  1 for M <= 16.  -1 on bad sizes. */
+ * at most 16.  The output tiles are those of the fused GEMM's tile height
+ * for this shape and CU count (64, 128 or 160 rows x 384 channels, the
+ * height with the least estimated time).  1 for M <= 16.  -1 on bad
+ * sizes. */
 int32_t s3d8_splitk_auto(int64_t M, int64_t K, int64_t N, int32_t num_cus);
 
 /* Workspace bytes of s3d8_linear_splitk at a split count >= 1 (0 for M <= 16
