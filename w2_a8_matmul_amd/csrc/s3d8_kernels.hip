@@ -896,8 +896,12 @@ __device__ __forceinline__ void gemv_stream_body(
     };
     // the first kEarly entries now, the rest after the workgroup barrier
     // below: a wave stalled issuing weight loads behind the memory
-    // system's backlog reaches its absmax late and holds up the barrier
-    constexpr int kEarly = 2;
+    // system's backlog reaches its absmax late and holds up the barrier.
+    // Measured at K = 4096, N = 14336: one token row 6.77 us with three
+    // entries early against 6.97 with two (7.35 with one, 7.20 with four;
+    // also faster for 3D8, the lm_head and the batched layer); four rows
+    // 10.43 us with two against 10.57 with three.
+    constexpr int kEarly = MR == 1 ? 3 : 2;
 #pragma unroll
     for (int sl = 0; sl < kEarly; ++sl) {
         asm volatile("" : "=v"(pr[sl]));  // defined, with no code: the load below overwrites it
