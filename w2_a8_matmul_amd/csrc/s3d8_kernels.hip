@@ -207,11 +207,14 @@ __device__ __forceinline__ void load_block_to_lds(const uint32_t (&lds)[NA + 2],
 // lane-interleaved signed table.  S3D8: the 96-byte centroid table, read
 // through the scalar cache so that it does not queue behind vector loads
 // already in flight; 3D8 (f3d8): the 768-byte signed table, one word per
-// thread.  C32 must be 4-byte aligned.  Contains barriers.
+// thread.  C32 must be 4-byte aligned.  Contains barriers.  kThreads: the
+// workgroup size (a constant, so that no load of it from the argument
+// segment is waited for first)
+template <int kThreads>
 __device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *clw, const uint32_t *__restrict__ C32,
                                                       bool f3d8) {
     if (f3d8) {
-        for (int i = threadIdx.x; i < kTableWords3D8; i += blockDim.x) clw[i] = C32[i];
+        for (int i = threadIdx.x; i < kTableWords3D8; i += kThreads) clw[i] = C32[i];
     } else {
         uint32_t cw[24];
 #pragma unroll
@@ -224,7 +227,7 @@ __device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *c
     }
     __syncthreads();
     const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
-    for (int idx = threadIdx.x; idx < kTabWords / 4; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < kTabWords / 4; idx += kThreads) {
         const uint32_t b = (uint32_t)idx >> 4;
         const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
         reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
@@ -1207,11 +1210,14 @@ constexpr int kCodesWaveBytes = 4096;  // codes per wave: M * 64 * kbw <= 4096
 constexpr int kCodesMaxTiles = 16;
 constexpr int kCodesSlots = 4;
 
+// (the arguments used before the first loads come first, the grid size
+// among them, so that all of them are preloaded into SGPRs: gridDim.x would
+// be a load from the argument segment, waited for before any other load)
 template <int MR, int NCL, bool F3>
 __global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
                                                           const uint8_t *__restrict__ tiled,
                                                           const uint8_t *__restrict__ table,
-                                                          const uint16_t *__restrict__ scales, int K, int N,
+                                                          const uint16_t *__restrict__ scales, int K, int N, int grid,
                                                           int ntw_q, int ntw_r, void *__restrict__ y,
                                                           int32_t *__restrict__ acc_out, int obf) {
     static_assert(MR >= 1 && MR <= kCodesMaxRows, "1 to 8 token rows");
@@ -1232,7 +1238,7 @@ __global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restri
     const int T = (N + 2) / 3, KB = (K + 63) >> 6, tiles = (T + 15) >> 4;
     const int kbw = (KB + W - 1) / W;
     const int kb0 = wave * kbw;
-    const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
+    const int bid = (int)blockIdx.x;
     const int ntw = ntw_q + (bid < ntw_r);  // tiles of this workgroup, >= 1
     const int nout = ntw * MR * 48;
 
@@ -1665,13 +1671,15 @@ constexpr uint32_t kPartQuad = 1024;  // one 16-byte quarter of an accumulator, 
 constexpr int kSpinLimit = 1 << 20;   // about 0.2 s of s_sleep 8
 __host__ __device__ constexpr uint32_t part_wave_bytes(int rt) { return 3u * 4u * kPartQuad * (uint32_t)rt; }
 
+// (the arguments the prologue uses come first, so that they are all among
+// the 16 argument dwords preloaded into SGPRs; the epilogue's follow)
 template <int RT, bool kAcc, bool kBF, bool kSplit>
-__global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                   int M, int K, int N, int T, const uint8_t *__restrict__ tiled,
-                                                   const uint32_t *__restrict__ centroids,
+__global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq, const uint8_t *__restrict__ tiled,
+                                                   const uint32_t *__restrict__ centroids, int M, int K, int N,
+                                                   int T, int nbm, int nbn, int f3d8, int splits, int kbper,
+                                                   const float *__restrict__ xs,
                                                    const uint16_t *__restrict__ scales, void *__restrict__ y,
-                                                   int32_t *__restrict__ acc_out, int nbm, int nbn, int f3d8,
-                                                   int splits, int kbper, int32_t *__restrict__ ws_cnt,
+                                                   int32_t *__restrict__ acc_out, int32_t *__restrict__ ws_cnt,
                                                    int32_t *__restrict__ ws_part, uint32_t part_bytes) {
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     constexpr int BM = 32 * RT;          // token rows per workgroup
@@ -2103,7 +2111,7 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
     int64_t nchunks, int8_t *__restrict__ w, int f3d8) {
     __shared__ uint32_t tab[kTabWords];
     __shared__ uint32_t clw[kTableWords3D8];
-    stage_and_build_table(tab, clw, centroids, f3d8 != 0);
+    stage_and_build_table<kDequantThreads>(tab, clw, centroids, f3d8 != 0);
     const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
     const int cpr = K >> 4;  // 16-byte chunks per triple row
     for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
@@ -2136,15 +2144,17 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_kernel(
 // written: they only meet zero activations or outputs that are never
 // stored.  Thread c handles 16-byte chunk c of the tiled matrix: fragment
 // c / 64, lane c % 64 = triple n + 16 g of the fragment, columns 16 g ..
+// (grid = gridDim.x, passed so that it arrives preloaded with the other
+// arguments instead of through a load from the argument segment)
 __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
-    const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids, int K, int T, int KB,
+    const uint8_t *__restrict__ tiled, const uint32_t *__restrict__ centroids, int K, int T, int KB, int grid,
     int64_t nchunks, int8_t *__restrict__ w8, int f3d8) {
     __shared__ uint32_t tab[kTabWords];
     __shared__ uint32_t clw[kTableWords3D8];
-    stage_and_build_table(tab, clw, centroids, f3d8 != 0);
+    stage_and_build_table<kDequantThreads>(tab, clw, centroids, f3d8 != 0);
     const uint32_t lane_off = (uint32_t)(threadIdx.x & 63) << 2;
     for (int64_t c = (int64_t)blockIdx.x * kDequantThreads + threadIdx.x; c < nchunks;
-         c += (int64_t)gridDim.x * kDequantThreads) {
+         c += (int64_t)grid * kDequantThreads) {
         const int64_t frag = c >> 6;
         const int l = (int)(c & 63);
         const int64_t tile = frag / KB;
@@ -2185,10 +2195,11 @@ __device__ __forceinline__ void vm_wait_imm_barrier() {
 }
 
 template <int RT, bool kAcc, bool kBF>
-__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const float *__restrict__ xs,
-                                                      int M, int K, int N, int NP, const int8_t *__restrict__ w8,
+__global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const int8_t *__restrict__ w8,
+                                                      int M, int K, int N, int NP, int nbm, int nbn,
+                                                      const float *__restrict__ xs,
                                                       const uint16_t *__restrict__ scales, void *__restrict__ y,
-                                                      int32_t *__restrict__ acc_out, int nbm, int nbn) {
+                                                      int32_t *__restrict__ acc_out) {
     static_assert(RT == 4 || RT == 5, "4 or 5 row tiles per wave");
     constexpr int BM = 32 * RT;
     constexpr int kSlots = RT == 4 ? 5 : 4;
@@ -2628,7 +2639,7 @@ bool launch_gemv_codes(const int8_t *xq, const float *xs, int64_t M, int64_t K, 
     const int64_t grid = tiles < cus ? tiles : cus;
     if ((tiles + grid - 1) / grid > kCodesMaxTiles) return false;
     typedef void (*CodesFn)(const int8_t *, const float *, const uint8_t *, const uint8_t *, const uint16_t *, int,
-                            int, int, int, void *, int32_t *, int);
+                            int, int, int, int, void *, int32_t *, int);
     // 16-byte code loads per lane: M * 4 * kbw chunks over 64 lanes (1, 2 or 4)
     const int64_t ncl = (M * 4 * kbw + 63) / 64;
     const int cl = ncl <= 1 ? 0 : ncl <= 2 ? 1 : 2;
@@ -2639,7 +2650,7 @@ bool launch_gemv_codes(const int8_t *xq, const float *xs, int64_t M, int64_t K, 
 #undef S3D8_CODES_ROWS
 #undef S3D8_CODES
     hipLaunchKernelGGL(fns[f3d8 ? 1 : 0][M - 1][cl], dim3((unsigned)grid), dim3(1024), 0, stream, xq, xs, tiled,
-                       static_cast<const uint8_t *>(table), scales, (int)K, (int)N, (int)(tiles / grid),
+                       static_cast<const uint8_t *>(table), scales, (int)K, (int)N, (int)grid, (int)(tiles / grid),
                        (int)(tiles % grid), y, acc_out, (int)obf);
     return true;
 }
@@ -2765,8 +2776,8 @@ int gemm_auto_splits(int64_t M, int64_t K, int64_t N, int cus) {
     return best;
 }
 
-typedef void (*GemmFn)(const int8_t *, const float *, int, int, int, int, const uint8_t *, const uint32_t *,
-                       const uint16_t *, void *, int32_t *, int, int, int, int, int, int32_t *, int32_t *, uint32_t);
+typedef void (*GemmFn)(const int8_t *, const uint8_t *, const uint32_t *, int, int, int, int, int, int, int, int, int,
+                       const float *, const uint16_t *, void *, int32_t *, int32_t *, int32_t *, uint32_t);
 
 // Enqueue the fused GEMM under plan p (workspace checked by the caller).
 int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_t N,
@@ -2785,8 +2796,8 @@ int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M,
     int32_t *part = split ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.ws_cnt_bytes) : nullptr;
     hipLaunchKernelGGL(fns[split][p.rt == 2 ? 0 : p.rt == 4 ? 1 : 2][acc_out != nullptr][obf], dim3((unsigned)p.grid),
                        dim3(256), 0, stream,
-                       xq, xs, (int)M, (int)K, (int)N, (int)((N + 2) / 3), tiled, table32, scales_bf16, y, acc_out,
-                       p.nbm, p.nbn, (int)f3d8, p.splits, p.kbper, cnt, part, (uint32_t)p.ws_part_bytes);
+                       xq, tiled, table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn, (int)f3d8,
+                       p.splits, p.kbper, xs, scales_bf16, y, acc_out, cnt, part, (uint32_t)p.ws_part_bytes);
     return launch_status();
 }
 
@@ -3092,8 +3103,8 @@ int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_
     int64_t blocks = (nchunks + kDequantThreads - 1) / kDequantThreads;
     if (blocks > (int64_t)cus * 2) blocks = (int64_t)cus * 2;
     hipLaunchKernelGGL(dequant_tiled_kernel, dim3((unsigned)blocks), dim3(kDequantThreads), 0, (hipStream_t)stream,
-                       tiled, reinterpret_cast<const uint32_t *>(table), (int)K, (int)T, KB, nchunks, workspace,
-                       (int)f3d8);
+                       tiled, reinterpret_cast<const uint32_t *>(table), (int)K, (int)T, KB, (int)blocks, nchunks,
+                       workspace, (int)f3d8);
     const int nbn = (int)((3 * T + 383) / 384);
     // 4 or 5 row tiles per wave: the one that needs fewer workgroup rounds,
     // counted in units of row-tile work (this kernel has no 64-row build)
@@ -3106,15 +3117,15 @@ int unfused_impl(const int8_t *xq, const float *xs, int64_t M, int64_t K, int64_
     const int64_t nwg = (int64_t)nbm * nbn;
     const int64_t grid = (nwg + kXcds - 1) / kXcds * kXcds;
     if (grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-    typedef void (*I8Fn)(const int8_t *, const float *, int, int, int, int, const int8_t *, const uint16_t *, void *,
-                         int32_t *, int, int);
+    typedef void (*I8Fn)(const int8_t *, const int8_t *, int, int, int, int, int, int, const float *,
+                         const uint16_t *, void *, int32_t *);
     static const I8Fn fns[2][2][2] = {
         {{gemm_i8_kernel<4, false, false>, gemm_i8_kernel<4, false, true>},
          {gemm_i8_kernel<4, true, false>, gemm_i8_kernel<4, true, true>}},
         {{gemm_i8_kernel<5, false, false>, gemm_i8_kernel<5, false, true>},
          {gemm_i8_kernel<5, true, false>, gemm_i8_kernel<5, true, true>}}};
-    hipLaunchKernelGGL(fns[rt == 5][acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq, xs,
-                       (int)M, (int)K, (int)N, (int)(3 * T), workspace, scales_bf16, y, acc_out, nbm, nbn);
+    hipLaunchKernelGGL(fns[rt == 5][acc_out != nullptr][obf], dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, xq,
+                       workspace, (int)M, (int)K, (int)N, (int)(3 * T), nbm, nbn, xs, scales_bf16, y, acc_out);
     return launch_status();
 }
 
