@@ -1225,7 +1225,11 @@ __global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restri
     constexpr int W = 16, kThreads = W * 64;
     constexpr int NG = MR > 5 ? 2 : 1;  // row groups of the sparse product (five tokens each)
     constexpr int kEp = (kCodesMaxTiles * MR * 48 + kThreads - 1) / kThreads;
-    constexpr int kEarly = 2;           // ring entries issued before the first barrier
+    // ring entries issued before the first barrier: measured at K = 4096,
+    // N = 14336 (alternating on one box) 7.13 / 7.79 / 9.14 us at M = 1 / 4 / 8
+    // with three, against 7.44 / 8.03 / 9.45 with two and 7.10 / 7.83 / 9.50
+    // with four
+    constexpr int kEarly = 3;
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     // codes slice per wave: NCL loads of 16 bytes per lane, 1024 NCL bytes
     __shared__ __attribute__((aligned(16))) int8_t xw[W][1024 * NCL];
