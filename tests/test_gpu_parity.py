@@ -90,8 +90,11 @@ def _edge_rows(K):
     return x
 
 
+# K up to 65536 runs the one-read build (the row held in registers), longer
+# rows (65552, 70000) the two-read build
 @pytest.mark.parametrize("M,K", [(1, 16), (1, 256), (3, 48), (8, 4096), (1, 14336), (37, 1280),
-                                 (1601, 5120), (2048, 4096), (6, 16384), (7, 16400), (2, 20000)])
+                                 (1601, 5120), (2048, 4096), (6, 16384), (7, 16400), (2, 20000),
+                                 (6, 65536), (1, 65552), (7, 70000)])
 def test_quant_act_matches_oracle(gpu, M, K):
     x = workloads.gaussian_matrix([2001, M, K], M, K)
     if M >= 6:

@@ -242,7 +242,10 @@ __device__ __forceinline__ void stage_and_build_table(uint32_t *tab, uint32_t *c
 // channel-scaled INT8 activations, one scale per token).  NV > 0: the row is
 // read once, NV float4 per thread held in registers between the reduction
 // and the quantisation (K <= 1024 NV); NV = 0: any K, the row is read twice.
-constexpr int kQuantThreads = 256;
+// (1024 threads: one float4 per thread at K = 4096, so the serial chain of
+// IEEE divisions per thread is short; 0.07 to 0.09 us faster than 256
+// threads at 1, 8 and 64 rows, K = 4096, alternating on one box)
+constexpr int kQuantThreads = 1024;
 
 template <int NV>
 __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *__restrict__ x, int K,
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_act_kernel(const float *_
 }
 
 // Launch of quant_act_kernel: the one-read build when the row fits 16
-// float4 per thread (K <= 16384), else the two-read build.
+// float4 per thread (K <= 65536), else the two-read build.
 void launch_quant_act(const float *x, int64_t M, int64_t K, int8_t *xq, float *xs, hipStream_t stream) {
     const int64_t nv = (K / 4 + kQuantThreads - 1) / kQuantThreads;
     typedef void (*QFn)(const float *, int, int8_t *, float *);
