@@ -1518,19 +1518,13 @@ __device__ __forceinline__ bool gemm_tile(int nbm, int nbn, int &bm, int &bn) {
 // the same followed by lgkmcnt(0) and a workgroup barrier.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N == 8 || N == 9 || N == 10 || N == 12 || N == 15, "add the immediate");
-    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    if constexpr (N == 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
-    static_assert(N == 6 || N == 8 || N == 10, "add the immediate");
-    if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    static_assert(N >= 0 && N <= 63, "vmcnt is a 6-bit count");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -2192,15 +2186,6 @@ __global__ __launch_bounds__(kDequantThreads) void dequant_tiled_kernel(
 // kSlots - 1 blocks ahead (five slots at RT = 4, four at RT = 5, whose
 // larger activation tile leaves room for no more); the MFMAs read both
 // operands from LDS.
-template <int N>
-__device__ __forceinline__ void vm_wait_imm() {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void vm_wait_imm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
 template <int RT, bool kAcc, bool kBF>
 __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__ xq, const int8_t *__restrict__ w8,
                                                       int M, int K, int N, int NP, int nbm, int nbn,
@@ -2327,7 +2312,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     // block kb + kAhead, read block kb + 1's operands into `nxt` while the
     // MFMAs of block kb run
     auto block = [&](const Ops &cur, Ops &nxt, int kb, int slot) {
-        vm_wait_imm_barrier<(kAhead - 2) * ND>();
+        wait_vmcnt_barrier<(kAhead - 2) * ND>();
         issue(kb + kAhead, slot == 0 ? kSlots - 1 : slot - 1);
         read_ops(nxt, slot == kSlots - 1 ? 0 : slot + 1);
         mfmas(cur);
@@ -2342,7 +2327,7 @@ __global__ __launch_bounds__(256) void gemm_i8_kernel(const int8_t *__restrict__
     };
 
     Ops o0, o1;
-    vm_wait_imm_barrier<(kAhead - 1) * ND>();  // block 0 in LDS for every wave
+    wait_vmcnt_barrier<(kAhead - 1) * ND>();  // block 0 in LDS for every wave
     read_ops(o0, 0);
     int kb = 0, slot = 0;
 #pragma unroll 1
