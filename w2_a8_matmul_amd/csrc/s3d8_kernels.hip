@@ -1649,10 +1649,12 @@ __device__ __forceinline__ void store_tile_rows(const v16i (&acc)[RT][3], const 
 // workgroups of a tile meet through two counters per tile in ws_cnt: each
 // takes an arrival number from the first and stores its partial sums in slot
 // `arrival` of the tile in ws_part (`splits` slots per tile,
-// part_wave_bytes(RT) per wave); all but the last then count themselves
-// done in the second; the last waits for splits - 1 done, sets both
-// counters back to zero for the next call, and runs the epilogue on the sum
-// of all slots.  It only waits for workgroups that have already arrived (so
+// part_wave_bytes(RT) per wave; on 64-row tiles the last arrival stores
+// nothing); all but the last then count themselves done in the second; the
+// last waits for splits - 1 done, sets both counters back to zero for the
+// next call, and runs the epilogue on the sum of all the tile's partial
+// sums.  It only waits
+// for workgroups that have already arrived (so
 // are running and wait for nothing), and the wait is bounded: counters that
 // do not start at zero give wrong results, never a hang.  Loads and stores
 // in ws_part are range-checked against part_bytes.
@@ -1943,34 +1945,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     // loads of blocks past the end are still in flight: drain before exit
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
+    // kKeepOwn: the last workgroup of a tile adds the other slots to its own
+    // accumulators (row tiles unrolled, so that the accumulators are indexed
+    // at compile time); otherwise it stores its sums like the others and
+    // adds all slots in a run-time row-tile loop.  Only the 64-row tiles
+    // take the first form: with 128 or 160 rows the compiler moves part of
+    // the accumulators through scratch memory for it, as much traffic as the
+    // slot it saves.  (Adding into the accumulators, or indexing them with a
+    // run-time row tile, made it spill inside the main loop.)
+    constexpr bool kKeepOwn = RT == 2;
     if (kSplit && splits > 1) {
-        // every workgroup of the tile stores its sums in slot `arrival`;
-        // the last then adds all slots (its own included, so that the
-        // accumulators are only ever read, as by the plain epilogue: adding
-        // into them here made the compiler move some out of the accumulator
-        // registers and spill inside the main loop)
         __shared__ int arrival;
         const int tile = bm * nbn + bn;
         if (tid == 0)
             arrival = __hip_atomic_fetch_add(ws_cnt + 2 * tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
         const int arr = min(max(arrival, 0), splits - 1);
-        const auto rp = make_rsrc(ws_part, part_bytes);
-        const uint32_t pb = ((uint32_t)(tile * splits + arr) * 4u + (uint32_t)wave) * part_wave_bytes(RT) + 16u * lane;
+        auto store_own = [&]() {
+            const auto rp = make_rsrc(ws_part, part_bytes);
+            const uint32_t pb =
+                ((uint32_t)(tile * splits + arr) * 4u + (uint32_t)wave) * part_wave_bytes(RT) + 16u * lane;
 #pragma unroll
-        for (int i = 0; i < RT; ++i)
+            for (int i = 0; i < RT; ++i)
 #pragma unroll
-            for (int d = 0; d < 3; ++d)
+                for (int d = 0; d < 3; ++d)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4i v{acc[i][d][4 * q], acc[i][d][4 * q + 1], acc[i][d][4 * q + 2], acc[i][d][4 * q + 3]};
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp,
-                                                           pb + (uint32_t)((i * 3 + d) * 4 + q) * kPartQuad, 0,
-                                                           kScopeDevice);
-                }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's sums are stored at device scope
-        __syncthreads();
+                    for (int q = 0; q < 4; ++q) {
+                        const v4i v{acc[i][d][4 * q], acc[i][d][4 * q + 1], acc[i][d][4 * q + 2],
+                                    acc[i][d][4 * q + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), rp,
+                                                               pb + (uint32_t)((i * 3 + d) * 4 + q) * kPartQuad, 0,
+                                                               kScopeDevice);
+                    }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's sums are stored at device scope
+            __syncthreads();
+        };
+        if constexpr (!kKeepOwn) store_own();
         if (arr < splits - 1) {
+            if constexpr (kKeepOwn) store_own();
             if (tid == 0) __hip_atomic_fetch_add(ws_cnt + 2 * tile + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
@@ -2002,12 +2014,52 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
         return;
     }
     // split-K, last workgroup of the tile: one 32-row tile at a time, the
-    // sum of all slots, two slots' loads (24 per lane) in flight at a time
-    // (the loads come from other XCDs' writes at device scope: one at a time
-    // they cost about half a microsecond each)
+    // slots added to its own sums (kKeepOwn: slots 0 .. splits - 2 to the
+    // accumulators; else all slots, its own included, to zero), two slots'
+    // loads (24 per lane) in flight at a time (the loads come from other
+    // XCDs' writes at device scope: one at a time they cost about half a
+    // microsecond each)
     const auto rp = make_rsrc(ws_part, part_bytes);
     const int tile = bm * nbn + bn;
     const int rows = min(RT, (M - row0 + 31) / 32);
+    if constexpr (kKeepOwn) {
+#pragma unroll
+        for (int i = 0; i < RT; ++i) {
+            if (i >= rows) break;  // uniform
+            v16i sum[1][3] = {{acc[i][0], acc[i][1], acc[i][2]}};
+#pragma unroll 1
+            for (int s = 0; s < splits - 1; s += 2) {
+                uint4 v[2][12];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    // a missing second slot reads zeros (out-of-range offset)
+                    const uint32_t pb = s + u < splits - 1
+                                            ? ((uint32_t)(tile * splits + s + u) * 4u + (uint32_t)wave) *
+                                                      part_wave_bytes(RT) +
+                                                  16u * lane + (uint32_t)(12 * i) * kPartQuad
+                                            : kOOB;
+#pragma unroll
+                    for (int j = 0; j < 12; ++j)
+                        v[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                rp, pb == kOOB ? kOOB : pb + (uint32_t)j * kPartQuad,
+                                                                0, kScopeDevice));
+                }
+                __builtin_amdgcn_sched_barrier(0);  // all 24 loads issued before the first add waits
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+#pragma unroll
+                    for (int j = 0; j < 12; ++j) {
+                        const int d = j >> 2, q = j & 3;
+                        sum[0][d][4 * q] += (int32_t)v[u][j].x;
+                        sum[0][d][4 * q + 1] += (int32_t)v[u][j].y;
+                        sum[0][d][4 * q + 2] += (int32_t)v[u][j].z;
+                        sum[0][d][4 * q + 3] += (int32_t)v[u][j].w;
+                    }
+            }
+            store_tile_rows<true, kAcc, 1, kBF>(sum, xs, M, N, row0 + 32 * i, h, sc, coff, y, acc_out);
+        }
+        return;
+    }
 #pragma unroll 1
     for (int i = 0; i < rows; ++i) {
         v16i sum[1][3] = {};
