@@ -11,7 +11,11 @@ Runs, in one process and in this order:
      150 warm-up launches (the clocks settle under sustained load), then 4
      launches: the summaries use the last 4 dispatches;
   4. the same problem through s3d8_linear_unfused (dequant_tiled_kernel +
-     gemm_i8_kernel), 4 calls.
+     gemm_i8_kernel), 4 calls;
+  5. ``gemv_codes_c1_m8``: s3d8_linear at M=8 on the decode GEMV shape (the
+     GEMV on INT8 codes), 28 weight copies, 2 passes;
+  6. ``splitk_vision_down``: s3d8_linear_splitk on M=1601, K=5120, N=1280 at
+     the library's split count, 50 warm-up launches, then 4.
 Weights are random S3D8 formats (uniform bytes, random table and scales):
 the bytes moved do not depend on the values.
 
@@ -89,6 +93,32 @@ def main() -> None:
         s3d8.linear_unfused(xq, xs, tiled, C, S, N, workspace=ws, y=y)
     torch.cuda.synchronize()
     say(f"gemm_c3 unfused: 4 calls of s3d8_linear_unfused M={M} K={K} N={N}")
+    del ws, tiled, y
+
+    # 5. the GEMV on INT8 codes, eight tokens
+    M = 8
+    C, S, tiled = fmt(13, N, K)
+    copies = [tiled.clone() for _ in range(28)]
+    xq, xs = s3d8.quant_act(torch.randn((M, K), dtype=torch.float32, device=dev))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        for t in copies:
+            s3d8.linear(xq, xs, t, C, S, N, y=y)
+    torch.cuda.synchronize()
+    say(f"gemv_codes_c1_m8: {2 * len(copies)} launches of s3d8_linear M={M} K={K} N={N}")
+    del copies, tiled
+
+    # 6. split-K on the vision down-projection
+    M, K, N = 1601, 5120, 1280
+    C, S, tiled = fmt(14, N, K)
+    xq, xs = s3d8.quant_act(torch.randn((M, K), dtype=torch.float32, device=dev))
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    splits = s3d8.splitk_auto(M, K, N, torch.cuda.get_device_properties(dev).multi_processor_count)
+    wsk = torch.zeros((max(1, s3d8.splitk_workspace_bytes(M, K, N, splits)),), dtype=torch.uint8, device=dev)
+    for _ in range(50 + 4):
+        s3d8.linear_splitk(xq, xs, tiled, C, S, N, splits=splits, workspace=wsk, y=y)
+    torch.cuda.synchronize()
+    say(f"splitk_vision_down: 50 + 4 launches of s3d8_linear_splitk M={M} K={K} N={N} splits={splits}")
 
 
 if __name__ == "__main__":
