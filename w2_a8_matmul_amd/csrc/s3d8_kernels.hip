@@ -2103,6 +2103,315 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
     }
 }
 
+// --------------------------------------------------------------- GEMM, eight waves
+
+// The fused GEMM's 160-row workgroup tile (160 token rows x 128 triples)
+// split by columns over eight waves, two per SIMD: wave w owns weight
+// fragment w of the tile (16 triples, 48 channels) over all 160 rows, on
+// v_mfma_i32_16x16x64_i8: 10 row tiles x the 3 channels of the triple = 30
+// accumulators of 16 x 16 (120 registers).  Each wave decodes only its own
+// fragment (16 table lookups per lane and block, half of gemm_kernel's at
+// the same tile) and reads the whole activation tile (10 ds_read_b128 per
+// block).  With two waves per SIMD one wave's lookups, reads and decode run
+// beside the other wave's MFMAs, which one wave per SIMD cannot do.
+//
+// Operand layouts of the 16 x 16 x 64 product: B lane (t, g) = t + 16 g
+// holds column t at k = 16 g .. 16 g + 15, which is how the tiled layout
+// stores a fragment's block (one ds_read_b128 at 16 lane gives a wave its
+// raw weights); A lane (r, g) holds row r of the row tile, 16-byte chunk g of
+// the block; the result lane (t, g) holds triple t for rows 4 g .. 4 g + 3.
+//
+// Copies as in gemm_kernel (LDS-DMA, five slots, four blocks ahead, the same
+// swizzled activation tile): the 10 activation loads and 8 weight loads of a
+// block go to waves w (activation load w and weight load w) and, for w < 2,
+// activation load 8 + w as well.
+constexpr int kW8Rows = 10;  // row tiles of 16: 160 token rows
+constexpr int kW8Threads = 512;
+
+// Epilogue of the eight-wave GEMM for one wave: y[row][3 t + d] = (xs[row] *
+// acc) * sc[d] for rows 16 i + 4 g + v of accumulator acc[i][d] (element v);
+// coff[d] is the byte offset of channel 3 t + d within a row of y (kOOB
+// past N).  Branch-free as store_tile_rows: rows past M and channels past N
+// get an out-of-range offset and their stores are dropped; a lane whose
+// triple straddles N stores its valid channels one by one in a second pass.
+// kBF: bfloat16 outputs, one 2-byte store per channel.
+template <bool kAcc, bool kBF>
+__device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const float *__restrict__ xs, int M, int N,
+                                             int row0, int g, const float (&sc)[3], const uint32_t (&coff)[3],
+                                             void *__restrict__ y, int32_t *__restrict__ acc_out) {
+    const int nrows = min(M - row0, 16 * kW8Rows);
+    const uint32_t rowb = 4u * (uint32_t)N;
+    const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
+    float4 sx[kW8Rows];
+#pragma unroll
+    for (int i = 0; i < kW8Rows; ++i) sx[i] = __builtin_bit_cast(float4, bload16(rxs, 4u * (uint32_t)(16 * i + 4 * g)));
+    const auto ra = make_rsrc(acc_out + (int64_t)row0 * N, kAcc ? rowb * (uint32_t)nrows : 0u);
+    auto dead = [&](int r) { return (uint32_t)(nrows - 1 - r) & kOOB; };
+    auto outf = [&](int i, int v, int d) { return (sx[i][v] * (float)acc[i][d][v]) * sc[d]; };
+    auto out = [&](int i, int v, int d) { return __float_as_uint(outf(i, v, d)); };
+    if constexpr (kBF) {
+        const uint32_t yrowb = 2u * (uint32_t)N;
+        const auto ry = make_rsrc(static_cast<uint16_t *>(y) + (int64_t)row0 * N, yrowb * (uint32_t)nrows);
+#pragma unroll
+        for (int i = 0; i < kW8Rows; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * g + v;
+#pragma unroll
+                for (int d = 0; d < 3; ++d) {
+                    const uint32_t yo = coff[d] == kOOB ? kOOB : coff[d] >> 1;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(outf(i, v, d)), ry,
+                                                          (yo + (uint32_t)r * yrowb) | dead(r), 0, 0);
+                    if constexpr (kAcc)
+                        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][d][v], ra,
+                                                              (coff[d] + (uint32_t)r * rowb) | dead(r), 0, 0);
+                }
+            }
+        return;
+    }
+    typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+    const auto ry = make_rsrc(static_cast<float *>(y) + (int64_t)row0 * N, rowb * (uint32_t)nrows);
+    const bool split = coff[0] != kOOB && coff[2] == kOOB;
+    const uint32_t base3 = split ? kOOB : coff[0];
+#pragma unroll
+    for (int i = 0; i < kW8Rows; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * i + 4 * g + v;
+            const uint32_t off = (base3 + (uint32_t)r * rowb) | dead(r);
+            __builtin_amdgcn_raw_buffer_store_b96(u3{out(i, v, 0), out(i, v, 1), out(i, v, 2)}, ry, off, 0, 0);
+            if constexpr (kAcc)
+                __builtin_amdgcn_raw_buffer_store_b96(
+                    u3{(uint32_t)acc[i][0][v], (uint32_t)acc[i][1][v], (uint32_t)acc[i][2][v]}, ra, off, 0, 0);
+        }
+    if (__builtin_amdgcn_ballot_w64(split) == 0) return;
+#pragma unroll
+    for (int i = 0; i < kW8Rows; ++i)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int r = 16 * i + 4 * g + v;
+            const uint32_t dd = dead(r) | (split ? 0u : kOOB);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                const uint32_t off = (coff[d] + (uint32_t)r * rowb) | dd;
+                __builtin_amdgcn_raw_buffer_store_b32(out(i, v, d), ry, off, 0, 0);
+                if constexpr (kAcc) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][d][v], ra, off, 0, 0);
+            }
+        }
+}
+
+// vmcnt waits of the eight-wave GEMM, where waves 0 and 1 issue three loads
+// per block and the others two: wait until at most `blocks` blocks of this
+// wave's loads are in flight (then, kBar, lgkmcnt(0) and a workgroup barrier)
+template <int kBlocks, bool kBar>
+__device__ __forceinline__ void w8_wait(int wave) {
+    if (wave < 2) {
+        if constexpr (kBar) wait_vmcnt_barrier<3 * kBlocks>(); else wait_vmcnt<3 * kBlocks>();
+    } else {
+        if constexpr (kBar) wait_vmcnt_barrier<2 * kBlocks>(); else wait_vmcnt<2 * kBlocks>();
+    }
+}
+
+template <bool kAcc, bool kBF>
+__global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__restrict__ xq,
+                                                             const uint8_t *__restrict__ tiled,
+                                                             const uint32_t *__restrict__ centroids, int M, int K,
+                                                             int N, int T, int nbm, int nbn, int f3d8,
+                                                             const float *__restrict__ xs,
+                                                             const uint16_t *__restrict__ scales,
+                                                             void *__restrict__ y, int32_t *__restrict__ acc_out) {
+    constexpr int BM = 16 * kW8Rows;
+    __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
+    __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][BM * 64];
+    __shared__ __attribute__((aligned(16))) int8_t wbuf[kGemmSlots][kGemmBF * 1024];
+    __shared__ uint32_t clw[kTableWords3D8];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int KB = (K + 63) >> 6;
+    const int tiles16 = (T + 15) >> 4;
+    const uint32_t lane_off = (uint32_t)lane << 2;
+
+    int bm, bn;
+    if (!gemm_tile(nbm, nbn, bm, bn)) return;  // padding workgroup (grid rounded up to a multiple of 8)
+    const int row0 = bm * BM;
+    const int frag = bn * kGemmBF + wave;
+
+    uint32_t cw[24];
+#pragma unroll
+    for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+    uint32_t c3;
+    {
+        const v4i rc3 = rsrc_words(centroids, 768u);
+        const uint32_t off = (f3d8 && tid < kTableWords3D8) ? 4u * (uint32_t)tid : kOOB;
+        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(c3) : "v"(off), "s"(rc3) : "memory");
+    }
+
+    const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
+    const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
+
+    // activation loads of this wave: load index L = wave (+ 8 for waves 0
+    // and 1) moves rows 16 L .. 16 L + 15; lane l takes row 16 L + l / 4,
+    // chunk (l % 4) ^ ((row / 4) % 4), stored at 16 l of the load's KiB
+    uint32_t aoff[2], atail[2];
+    const int ktail = K - 64 * (KB - 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * (wave + 8 * j) + (lane >> 2);
+        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        aoff[j] = (j == 0 || wave < 2) && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        atail[j] = 16 * chunk < ktail ? aoff[j] : kOOB;
+    }
+    // weight load: the wave's own fragment, 16 bytes per lane in place
+    const uint32_t woff = frag < tiles16 ? (uint32_t)frag * (uint32_t)KB * 1024u + 16u * lane : kOOB;
+    const uint32_t abase = S3D8_LDS_OFFSET(&abuf[0][0]), wbase = S3D8_LDS_OFFSET(&wbuf[0][0]);
+    // blocks past the end re-read the last block into a slot never read, so
+    // that every wait counts the same
+    auto issue = [&](int kb, int slot) {
+        const int kbc = kb < KB ? kb : KB - 1;
+        const bool tail = kbc >= KB - 1;
+        const uint32_t ab = abase + (uint32_t)(BM * 64) * slot;
+        load_to_lds16_so(ab + 1024u * wave, tail ? atail[0] : aoff[0], 64u * (uint32_t)kbc, rx);
+        if (wave < 2) load_to_lds16_so(ab + 1024u * (8 + wave), tail ? atail[1] : aoff[1], 64u * (uint32_t)kbc, rx);
+        load_to_lds16_so(wbase + (uint32_t)(kGemmBF * 1024) * slot + 1024u * wave, woff, 1024u * (uint32_t)kbc, rw);
+    };
+
+    // A operand of row tile i: row 16 i + l % 16, chunk l / 16 (swizzled)
+    const int ard = (lane & 15) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
+    auto read_a = [&](int slot, int i) { return *reinterpret_cast<const v4i *>(&abuf[slot][1024 * i + ard]); };
+    auto read_w = [&](int slot) { return *reinterpret_cast<const uint4 *>(&wbuf[slot][1024 * wave + 16 * lane]); };
+    // decode of raw dword c (k = 16 g + 4 c .. + 3): four table lookups, then
+    // the 4 x 3 byte transpose into dword c of the three B operands
+    auto lookups = [&](const uint4 &w, int c, uint32_t (&q)[4]) {
+        const char *tb = reinterpret_cast<const char *>(tab);
+        const uint32_t dw = c == 0 ? w.x : c == 1 ? w.y : c == 2 ? w.z : w.w;
+        q[0] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0400u));
+        q[1] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0500u));
+        q[2] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0600u));
+        q[3] = *reinterpret_cast<const uint32_t *>(tb + __builtin_amdgcn_perm(dw, lane_off, 0x0C0C0700u));
+    };
+    auto transpose = [&](const uint32_t (&q)[4], v4i (&b)[3], int c) {
+        const uint32_t p01 = __builtin_amdgcn_perm(q[1], q[0], 0x05010400u);
+        const uint32_t p23 = __builtin_amdgcn_perm(q[3], q[2], 0x05010400u);
+        const uint32_t s01 = __builtin_amdgcn_perm(q[1], q[0], 0x0C0C0602u);
+        const uint32_t s23 = __builtin_amdgcn_perm(q[3], q[2], 0x0C0C0602u);
+        b[0][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x05040100u);
+        b[1][c] = (int32_t)__builtin_amdgcn_perm(p23, p01, 0x07060302u);
+        b[2][c] = (int32_t)__builtin_amdgcn_perm(s23, s01, 0x05040100u);
+    };
+
+    // prologue as gemm_kernel's: blocks 0 and 1 in flight, the table, block 0
+    // waited for, then blocks 2 and 3
+    issue(0, 0);
+    issue(1, 1);
+    // (the table word is the oldest load; four younger loads in flight hold
+    // for every wave.  One wait for all waves, with no branch: a wave-dependent
+    // branch here let the compiler copy c3 before the wait.)
+    asm volatile("s_waitcnt vmcnt(4)" : "+v"(c3)::"memory");
+    if (f3d8) {
+        if (tid < kTableWords3D8) clw[tid] = c3;
+    } else if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i)
+            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+    }
+    __syncthreads();
+    {
+        const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
+        for (int idx = tid; idx < kTabWords / 4; idx += kW8Threads) {
+            const uint32_t b = (uint32_t)idx >> 4;
+            const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
+            reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
+        }
+    }
+    static_assert(kGemmAhead == 4, "the waits below assume four blocks in flight");
+    w8_wait<1, false>(wave);  // this wave's block 0 is in LDS
+    __syncthreads();          // everyone's block 0, and the table
+    issue(2, 2);
+    issue(3, 3);
+
+    v4i acc[kW8Rows][3];
+#pragma unroll
+    for (int i = 0; i < kW8Rows; ++i)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) acc[i][d] = v4i{0, 0, 0, 0};
+
+    // operands of block 0: A row tiles 0 and 1 (the rest are read during the
+    // block), B decoded
+    v4i an[2] = {read_a(0, 0), read_a(0, 1)};
+    v4i b0[3], b1[3];
+    {
+        const uint4 w0 = read_w(0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t q[4];
+            lookups(w0, c, q);
+            transpose(q, b0, c);
+        }
+    }
+
+    // block kb (slot `slot`): wait until blocks <= kb + 1 are in LDS for
+    // every wave, refill the slot of block kb - 1 with block kb + 4, then ten
+    // groups of three MFMAs (row tile i x the three B operands).  Group i
+    // reads A row tile i + 2 (of block kb + 1 for the last two groups); the
+    // raw weights of block kb + 1 come in group 0, their lookups in groups
+    // 2..5 and transposes in groups 6..9.
+    auto block = [&](v4i (&anx)[2], const v4i (&bc)[3], v4i (&bnx)[3], int kb, int slot) {
+        w8_wait<2, true>(wave);
+        const int next = slot == kGemmSlots - 1 ? 0 : slot + 1;
+        const int prev = slot == 0 ? kGemmSlots - 1 : slot - 1;
+        issue(kb + kGemmAhead, prev);
+        v4i a[kW8Rows];
+        a[0] = anx[0];
+        a[1] = anx[1];
+        uint4 wn;
+        uint32_t q[4][4];
+#pragma unroll
+        for (int i = 0; i < kW8Rows; ++i) {
+#pragma unroll
+            for (int d = 0; d < 3; ++d) acc[i][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bc[d], acc[i][d], 0, 0, 0);
+            if (i == 0) wn = read_w(next);
+            if (i + 2 < kW8Rows)
+                a[i + 2] = read_a(slot, i + 2);
+            else
+                anx[i + 2 - kW8Rows] = read_a(next, i + 2 - kW8Rows);
+            if (i >= 2 && i <= 5) lookups(wn, i - 2, q[i - 2]);
+            if (i >= 6) transpose(q[i - 6], bnx, i - 6);
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // a share of the VALU
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // and of the LDS reads
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    int kb = 0, slot = 0;
+#pragma unroll 1
+    for (; kb + 1 < KB; kb += 2) {
+        block(an, b0, b1, kb, slot);
+        slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
+        block(an, b1, b0, kb + 1, slot);
+        slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
+    }
+    if (kb < KB) block(an, b0, b1, kb, slot);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads of blocks past the end
+
+    // epilogue: lane (t, g) holds channels 3 (16 frag + t) + d
+    const int ch0 = 3 * (16 * frag + (lane & 15));
+    float sc[3];
+    uint32_t coff[3];
+    const auto rsc = make_rsrc(scales, (uint32_t)N * 2u);
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+        const bool ok = ch0 + d < N;
+        coff[d] = ok ? 4u * (uint32_t)(ch0 + d) : kOOB;
+        sc[d] = bf16_to_f32(bload2(rsc, ok ? 2u * (uint32_t)(ch0 + d) : kOOB));
+    }
+    store_rows16<kAcc, kBF>(acc, xs, M, N, row0, lane >> 4, sc, coff, y, acc_out);
+}
+
 // --------------------------------------------------------------- matrix-core rate probe
 
 // A measurement utility, not part of the method: the INT8 matrix-core rate
@@ -2843,6 +3152,16 @@ int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M,
 #undef S3D8_GEMM_BUILDS
 #undef S3D8_GEMM_RT
     const bool split = p.splits > 1;
+    if (p.rt == 5 && !split) {
+        typedef void (*W8Fn)(const int8_t *, const uint8_t *, const uint32_t *, int, int, int, int, int, int, int,
+                             const float *, const uint16_t *, void *, int32_t *);
+        static const W8Fn w8[2][2] = {{gemm_w8_kernel<false, false>, gemm_w8_kernel<false, true>},
+                                      {gemm_w8_kernel<true, false>, gemm_w8_kernel<true, true>}};
+        hipLaunchKernelGGL(w8[acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(kW8Threads), 0, stream, xq, tiled,
+                           table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn, (int)f3d8, xs,
+                           scales_bf16, y, acc_out);
+        return launch_status();
+    }
     int32_t *cnt = split ? static_cast<int32_t *>(ws) : nullptr;
     int32_t *part = split ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.ws_cnt_bytes) : nullptr;
     hipLaunchKernelGGL(fns[split][p.rt == 2 ? 0 : p.rt == 4 ? 1 : 2][acc_out != nullptr][obf], dim3((unsigned)p.grid),
