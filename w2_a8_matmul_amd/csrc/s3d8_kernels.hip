@@ -2105,13 +2105,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 
 // --------------------------------------------------------------- GEMM, eight waves
 
-// The fused GEMM's 160-row workgroup tile (160 token rows x 128 triples)
-// split by columns over eight waves, two per SIMD: wave w owns weight
-// fragment w of the tile (16 triples, 48 channels) over all 160 rows, on
-// v_mfma_i32_16x16x64_i8: 10 row tiles x the 3 channels of the triple = 30
-// accumulators of 16 x 16 (120 registers).  Each wave decodes only its own
+// The fused GEMM's workgroup tile (16 R token rows x 128 triples, R = 8 or
+// 10) split by columns over eight waves, two per SIMD: wave w owns weight
+// fragment w of the tile (16 triples, 48 channels) over all 16 R rows, on
+// v_mfma_i32_16x16x64_i8: R row tiles x the 3 channels of the triple = 3 R
+// accumulators of 16 x 16 (120 registers at R = 10).  Each wave decodes only its own
 // fragment (16 table lookups per lane and block, half of gemm_kernel's at
-// the same tile) and reads the whole activation tile (10 ds_read_b128 per
+// the same tile) and reads the whole activation tile (R ds_read_b128 per
 // block).  With two waves per SIMD one wave's lookups, reads and decode run
 // beside the other wave's MFMAs, which one wave per SIMD cannot do.
 //
@@ -2122,29 +2122,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 // the block; the result lane (t, g) holds triple t for rows 4 g .. 4 g + 3.
 //
 // Copies as in gemm_kernel (LDS-DMA, five slots, four blocks ahead, the same
-// swizzled activation tile): the 10 activation loads and 8 weight loads of a
-// block go to waves w (activation load w and weight load w) and, for w < 2,
-// activation load 8 + w as well.
-constexpr int kW8Rows = 10;  // row tiles of 16: 160 token rows
+// swizzled activation tile): the R activation loads and 8 weight loads of a
+// block go to waves w (activation load w and weight load w) and, for w + 8 <
+// R, activation load 8 + w as well.
 constexpr int kW8Threads = 512;
 
 // Epilogue of the eight-wave GEMM for one wave: y[row][3 t + d] = (xs[row] *
-// acc) * sc[d] for rows 16 i + 4 g + v of accumulator acc[i][d] (element v);
+// acc) * sc[d] for rows 16 i + 4 g + v of accumulator acc[i][d] (element v),
+// with xs[row0 + r] read from xsl[r] in LDS;
 // coff[d] is the byte offset of channel 3 t + d within a row of y (kOOB
 // past N).  Branch-free as store_tile_rows: rows past M and channels past N
 // get an out-of-range offset and their stores are dropped; a lane whose
 // triple straddles N stores its valid channels one by one in a second pass.
 // kBF: bfloat16 outputs, one 2-byte store per channel.
-template <bool kAcc, bool kBF>
-__device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const float *__restrict__ xs, int M, int N,
+template <int R, bool kAcc, bool kBF>
+__device__ __forceinline__ void store_rows16(const v4i (&acc)[R][3], const float *xsl, int M, int N,
                                              int row0, int g, const float (&sc)[3], const uint32_t (&coff)[3],
                                              void *__restrict__ y, int32_t *__restrict__ acc_out) {
-    const int nrows = min(M - row0, 16 * kW8Rows);
+    const int nrows = min(M - row0, 16 * R);
     const uint32_t rowb = 4u * (uint32_t)N;
-    const auto rxs = make_rsrc(xs + row0, 4u * (uint32_t)nrows);
-    float4 sx[kW8Rows];
+    float4 sx[R];
 #pragma unroll
-    for (int i = 0; i < kW8Rows; ++i) sx[i] = __builtin_bit_cast(float4, bload16(rxs, 4u * (uint32_t)(16 * i + 4 * g)));
+    for (int i = 0; i < R; ++i) sx[i] = *reinterpret_cast<const float4 *>(&xsl[16 * i + 4 * g]);
     const auto ra = make_rsrc(acc_out + (int64_t)row0 * N, kAcc ? rowb * (uint32_t)nrows : 0u);
     auto dead = [&](int r) { return (uint32_t)(nrows - 1 - r) & kOOB; };
     auto outf = [&](int i, int v, int d) { return (sx[i][v] * (float)acc[i][d][v]) * sc[d]; };
@@ -2153,7 +2152,7 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const
         const uint32_t yrowb = 2u * (uint32_t)N;
         const auto ry = make_rsrc(static_cast<uint16_t *>(y) + (int64_t)row0 * N, yrowb * (uint32_t)nrows);
 #pragma unroll
-        for (int i = 0; i < kW8Rows; ++i)
+        for (int i = 0; i < R; ++i)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int r = 16 * i + 4 * g + v;
@@ -2174,7 +2173,7 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const
     const bool split = coff[0] != kOOB && coff[2] == kOOB;
     const uint32_t base3 = split ? kOOB : coff[0];
 #pragma unroll
-    for (int i = 0; i < kW8Rows; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * i + 4 * g + v;
@@ -2186,7 +2185,7 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const
         }
     if (__builtin_amdgcn_ballot_w64(split) == 0) return;
 #pragma unroll
-    for (int i = 0; i < kW8Rows; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             const int r = 16 * i + 4 * g + v;
@@ -2200,19 +2199,21 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[kW8Rows][3], const
         }
 }
 
-// vmcnt waits of the eight-wave GEMM, where waves 0 and 1 issue three loads
-// per block and the others two: wait until at most `blocks` blocks of this
-// wave's loads are in flight (then, kBar, lgkmcnt(0) and a workgroup barrier)
-template <int kBlocks, bool kBar>
+// vmcnt waits of the eight-wave GEMM, where a wave issues one weight load
+// and one or two activation loads per block (two for w + 8 < R): wait until
+// at most kBlocks blocks of this wave's loads are in flight (then, kBar,
+// lgkmcnt(0) and a workgroup barrier)
+template <int R, int kBlocks, bool kBar>
 __device__ __forceinline__ void w8_wait(int wave) {
-    if (wave < 2) {
+    static_assert(R >= 8 && R <= 16, "every wave takes at least one activation load");
+    if (wave + 8 < R) {
         if constexpr (kBar) wait_vmcnt_barrier<3 * kBlocks>(); else wait_vmcnt<3 * kBlocks>();
     } else {
         if constexpr (kBar) wait_vmcnt_barrier<2 * kBlocks>(); else wait_vmcnt<2 * kBlocks>();
     }
 }
 
-template <bool kAcc, bool kBF>
+template <int R, bool kAcc, bool kBF>
 __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__restrict__ xq,
                                                              const uint8_t *__restrict__ tiled,
                                                              const uint32_t *__restrict__ centroids, int M, int K,
@@ -2220,11 +2221,13 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
                                                              const float *__restrict__ xs,
                                                              const uint16_t *__restrict__ scales,
                                                              void *__restrict__ y, int32_t *__restrict__ acc_out) {
-    constexpr int BM = 16 * kW8Rows;
+    static_assert(R == 8 || R == 10, "128 or 160 token rows (the block schedule and the LDS ring are sized for them)");
+    constexpr int BM = 16 * R;
     __shared__ __attribute__((aligned(16))) uint32_t tab[kTabWords];
     __shared__ __attribute__((aligned(16))) int8_t abuf[kGemmSlots][BM * 64];
     __shared__ __attribute__((aligned(16))) int8_t wbuf[kGemmSlots][kGemmBF * 1024];
     __shared__ uint32_t clw[kTableWords3D8];
+    __shared__ __attribute__((aligned(16))) float xsl[4 * 64];  // the tile's token scales (one LDS-DMA load)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -2237,15 +2240,11 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
     const int row0 = bm * BM;
     const int frag = bn * kGemmBF + wave;
 
-    uint32_t cw[24];
-#pragma unroll
-    for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
-    uint32_t c3;
-    {
-        const v4i rc3 = rsrc_words(centroids, 768u);
-        const uint32_t off = (f3d8 && tid < kTableWords3D8) ? 4u * (uint32_t)tid : kOOB;
-        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(c3) : "v"(off), "s"(rc3) : "memory");
-    }
+    // wave 0 copies the tile's token scales xs[row0 ..] into xsl first of all
+    // its loads (so that every later wait covers it); rows past M read zero
+    if (wave == 0)
+        load_to_lds16_so(S3D8_LDS_OFFSET(&xsl[0]), lane < 4 * R ? 16u * (uint32_t)lane : kOOB, 0u,
+                         rsrc_words(xs + row0, 4u * (uint32_t)(M - row0)));
 
     const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
     const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
@@ -2259,7 +2258,7 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
     for (int j = 0; j < 2; ++j) {
         const int row = 16 * (wave + 8 * j) + (lane >> 2);
         const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-        aoff[j] = (j == 0 || wave < 2) && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
+        aoff[j] = wave + 8 * j < R && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
         atail[j] = 16 * chunk < ktail ? aoff[j] : kOOB;
     }
     // weight load: the wave's own fragment, 16 bytes per lane in place
@@ -2272,7 +2271,7 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
         const bool tail = kbc >= KB - 1;
         const uint32_t ab = abase + (uint32_t)(BM * 64) * slot;
         load_to_lds16_so(ab + 1024u * wave, tail ? atail[0] : aoff[0], 64u * (uint32_t)kbc, rx);
-        if (wave < 2) load_to_lds16_so(ab + 1024u * (8 + wave), tail ? atail[1] : aoff[1], 64u * (uint32_t)kbc, rx);
+        if (wave + 8 < R) load_to_lds16_so(ab + 1024u * (8 + wave), tail ? atail[1] : aoff[1], 64u * (uint32_t)kbc, rx);
         load_to_lds16_so(wbase + (uint32_t)(kGemmBF * 1024) * slot + 1024u * wave, woff, 1024u * (uint32_t)kbc, rw);
     };
 
@@ -2301,38 +2300,53 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
     };
 
     // prologue as gemm_kernel's: blocks 0 and 1 in flight, the table, block 0
-    // waited for, then blocks 2 and 3
-    issue(0, 0);
-    issue(1, 1);
-    // (the table word is the oldest load; four younger loads in flight hold
-    // for every wave.  One wait for all waves, with no branch: a wave-dependent
-    // branch here let the compiler copy c3 before the wait.)
-    asm volatile("s_waitcnt vmcnt(4)" : "+v"(c3)::"memory");
+    // waited for, then blocks 2 and 3.  3D8: the 768-byte table as one word
+    // per thread, loaded before the blocks and waited for (oldest load, four
+    // younger ones in flight for every wave) in the same branch, so that its
+    // register is neither copied nor reused while the load is in flight;
+    // S3D8: the 96-byte table through the scalar cache, no vector wait.
     if (f3d8) {
+        uint32_t c3;
+        const uint32_t off = tid < kTableWords3D8 ? 4u * (uint32_t)tid : kOOB;
+        asm volatile("buffer_load_dword %0, %1, %2, 0 offen" : "=v"(c3) : "v"(off), "s"(rsrc_words(centroids, 768u))
+                     : "memory");
+        issue(0, 0);
+        issue(1, 1);
+        asm volatile("s_waitcnt vmcnt(4)" : "+v"(c3)::"memory");
         if (tid < kTableWords3D8) clw[tid] = c3;
-    } else if (tid == 0) {
+    } else {
+        uint32_t cw[24];
 #pragma unroll
-        for (int i = 0; i < 6; ++i)
-            reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
+        for (int i = 0; i < 24; ++i) cw[i] = centroids[i];
+        issue(0, 0);
+        issue(1, 1);
+        if (tid == 0)
+#pragma unroll
+            for (int i = 0; i < 6; ++i)
+                reinterpret_cast<uint4 *>(clw)[i] = make_uint4(cw[4 * i], cw[4 * i + 1], cw[4 * i + 2], cw[4 * i + 3]);
     }
     __syncthreads();
     {
+        // thread t computes entry t / 2 once and writes its copies
+        // 32 (t % 2) .. + 31 as eight 16-byte stores, in an order rotated by
+        // t / 2 so that the eight lanes of a store cycle hit distinct banks
+        static_assert(kW8Threads == 2 * kTabEntries && kTabCopies == 64, "two threads per table entry");
         const uint8_t *cl = reinterpret_cast<const uint8_t *>(clw);
-        for (int idx = tid; idx < kTabWords / 4; idx += kW8Threads) {
-            const uint32_t b = (uint32_t)idx >> 4;
-            const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
-            reinterpret_cast<uint4 *>(tab)[idx] = make_uint4(v, v, v, v);
-        }
+        const uint32_t b = (uint32_t)tid >> 1;
+        const uint32_t v = f3d8 ? row_3d8(b, cl) : signed_triple(b, cl);
+        uint4 *row = reinterpret_cast<uint4 *>(tab) + 16 * b + 8 * (tid & 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) row[(k + (tid >> 1)) & 7] = make_uint4(v, v, v, v);
     }
     static_assert(kGemmAhead == 4, "the waits below assume four blocks in flight");
-    w8_wait<1, false>(wave);  // this wave's block 0 is in LDS
+    w8_wait<R, 1, false>(wave);  // this wave's block 0 is in LDS
     __syncthreads();          // everyone's block 0, and the table
     issue(2, 2);
     issue(3, 3);
 
-    v4i acc[kW8Rows][3];
+    v4i acc[R][3];
 #pragma unroll
-    for (int i = 0; i < kW8Rows; ++i)
+    for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int d = 0; d < 3; ++d) acc[i][d] = v4i{0, 0, 0, 0};
 
@@ -2351,32 +2365,34 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
     }
 
     // block kb (slot `slot`): wait until blocks <= kb + 1 are in LDS for
-    // every wave, refill the slot of block kb - 1 with block kb + 4, then ten
+    // every wave, refill the slot of block kb - 1 with block kb + 4, then R
     // groups of three MFMAs (row tile i x the three B operands).  Group i
     // reads A row tile i + 2 (of block kb + 1 for the last two groups); the
-    // raw weights of block kb + 1 come in group 0, their lookups in groups
-    // 2..5 and transposes in groups 6..9.
+    // raw weights of block kb + 1 come in group 0, the lookups of raw dword c
+    // in group LK0 + c and its transpose in group R - 4 + c (LK0 = 2 at
+    // R = 10, 1 at R = 8: three groups between them either way).
     auto block = [&](v4i (&anx)[2], const v4i (&bc)[3], v4i (&bnx)[3], int kb, int slot) {
-        w8_wait<2, true>(wave);
+        w8_wait<R, 2, true>(wave);
         const int next = slot == kGemmSlots - 1 ? 0 : slot + 1;
         const int prev = slot == 0 ? kGemmSlots - 1 : slot - 1;
         issue(kb + kGemmAhead, prev);
-        v4i a[kW8Rows];
+        v4i a[R];
         a[0] = anx[0];
         a[1] = anx[1];
         uint4 wn;
         uint32_t q[4][4];
 #pragma unroll
-        for (int i = 0; i < kW8Rows; ++i) {
+        for (int i = 0; i < R; ++i) {
 #pragma unroll
             for (int d = 0; d < 3; ++d) acc[i][d] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], bc[d], acc[i][d], 0, 0, 0);
             if (i == 0) wn = read_w(next);
-            if (i + 2 < kW8Rows)
+            if (i + 2 < R)
                 a[i + 2] = read_a(slot, i + 2);
             else
-                anx[i + 2 - kW8Rows] = read_a(next, i + 2 - kW8Rows);
-            if (i >= 2 && i <= 5) lookups(wn, i - 2, q[i - 2]);
-            if (i >= 6) transpose(q[i - 6], bnx, i - 6);
+                anx[i + 2 - R] = read_a(next, i + 2 - R);
+            constexpr int LK0 = R >= 10 ? 2 : 1;
+            if (i >= LK0 && i < LK0 + 4) lookups(wn, i - LK0, q[i - LK0]);
+            if (i >= R - 4) transpose(q[i - (R - 4)], bnx, i - (R - 4));
 #pragma unroll
             for (int m = 0; m < 3; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -2396,9 +2412,9 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
         slot = slot == kGemmSlots - 1 ? 0 : slot + 1;
     }
     if (kb < KB) block(an, b0, b1, kb, slot);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads of blocks past the end
 
-    // epilogue: lane (t, g) holds channels 3 (16 frag + t) + d
+    // epilogue: lane (t, g) holds channels 3 (16 frag + t) + d (their scales
+    // loaded before the loads of blocks past the end are drained)
     const int ch0 = 3 * (16 * frag + (lane & 15));
     float sc[3];
     uint32_t coff[3];
@@ -2409,7 +2425,8 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
         coff[d] = ok ? 4u * (uint32_t)(ch0 + d) : kOOB;
         sc[d] = bf16_to_f32(bload2(rsc, ok ? 2u * (uint32_t)(ch0 + d) : kOOB));
     }
-    store_rows16<kAcc, kBF>(acc, xs, M, N, row0, lane >> 4, sc, coff, y, acc_out);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // loads of blocks past the end
+    store_rows16<R, kAcc, kBF>(acc, xsl, M, N, row0, lane >> 4, sc, coff, y, acc_out);
 }
 
 // --------------------------------------------------------------- matrix-core rate probe
@@ -3152,12 +3169,14 @@ int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M,
 #undef S3D8_GEMM_BUILDS
 #undef S3D8_GEMM_RT
     const bool split = p.splits > 1;
-    if (p.rt == 5 && !split) {
+    if ((p.rt == 4 || p.rt == 5) && !split) {
         typedef void (*W8Fn)(const int8_t *, const uint8_t *, const uint32_t *, int, int, int, int, int, int, int,
                              const float *, const uint16_t *, void *, int32_t *);
-        static const W8Fn w8[2][2] = {{gemm_w8_kernel<false, false>, gemm_w8_kernel<false, true>},
-                                      {gemm_w8_kernel<true, false>, gemm_w8_kernel<true, true>}};
-        hipLaunchKernelGGL(w8[acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(kW8Threads), 0, stream, xq, tiled,
+#define S3D8_W8(r) {{gemm_w8_kernel<r, false, false>, gemm_w8_kernel<r, false, true>}, \
+                    {gemm_w8_kernel<r, true, false>, gemm_w8_kernel<r, true, true>}}
+        static const W8Fn w8[2][2][2] = {S3D8_W8(8), S3D8_W8(10)};
+#undef S3D8_W8
+        hipLaunchKernelGGL(w8[p.rt == 5][acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(kW8Threads), 0, stream, xq, tiled,
                            table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn, (int)f3d8, xs,
                            scales_bf16, y, acc_out);
         return launch_status();
