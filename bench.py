@@ -569,7 +569,7 @@ def main():
                          "unit": "TOP/s", "frac": round(tops / INT8_PEAK_TOPS, 4),
                          "frac_of_probe": round(tops / ceilings["int8_mfma_probe_TOPS"], 4),
                          "traffic": measured_traffic("gemm_c3", None),
-                         "kernel": "gemm_kernel (fused decode + INT8 MFMA, via s3d8_linear)"},
+                         "kernel": "gemm_w8_kernel (fused decode + INT8 MFMA, eight waves, via s3d8_linear)"},
             "library_int8_gemm": lib_gemm,
             "unfused": {"value": round(u_tops, 2), "unit": "INT8 TOPS", "us_per_call": round(u_mean_us, 2),
                         "frac": round(u_tops / INT8_PEAK_TOPS, 4),

@@ -2121,10 +2121,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(const int8_t *__restrict__ xq
 // raw weights); A lane (r, g) holds row r of the row tile, 16-byte chunk g of
 // the block; the result lane (t, g) holds triple t for rows 4 g .. 4 g + 3.
 //
-// Copies as in gemm_kernel (LDS-DMA, five slots, four blocks ahead, the same
-// swizzled activation tile): the R activation loads and 8 weight loads of a
-// block go to waves w (activation load w and weight load w) and, for w + 8 <
-// R, activation load 8 + w as well.
+// Copies as in gemm_kernel (LDS-DMA, five slots, four blocks ahead): the R
+// activation loads and 8 weight loads of a block go to waves w (activation
+// load w and weight load w) and, for w + 8 < R, activation load 8 + w as
+// well.  The activation tile is laid out in LDS as the A operand wants it:
+// KiB i holds rows 16 i .. 16 i + 15, chunk g of row 16 i + r at 256 g + 16 r,
+// so that a row tile's operand is one contiguous ds_read_b128 (16 lane).
+// (gemm_kernel's row-swizzled layout, read in this operand's lane pattern,
+// measured a two-way bank conflict on every such read: SQ_LDS_BANK_CONFLICT
+// at a third of SQ_LDS_IDX_ACTIVE over the whole kernel.)
 constexpr int kW8Threads = 512;
 
 // Epilogue of the eight-wave GEMM for one wave: y[row][3 t + d] = (xs[row] *
@@ -2249,15 +2254,15 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
     const v4i rx = rsrc_words(xq, (uint32_t)M * (uint32_t)K);
     const v4i rw = rsrc_words(tiled, (uint32_t)tiles16 * (uint32_t)KB * 1024u);
 
-    // activation loads of this wave: load index L = wave (+ 8 for waves 0
-    // and 1) moves rows 16 L .. 16 L + 15; lane l takes row 16 L + l / 4,
-    // chunk (l % 4) ^ ((row / 4) % 4), stored at 16 l of the load's KiB
+    // activation loads of this wave: load index L = wave (+ 8 for w + 8 < R)
+    // moves rows 16 L .. 16 L + 15; lane l takes row 16 L + l % 16, chunk
+    // l / 16, stored at 16 l of the load's KiB
     uint32_t aoff[2], atail[2];
     const int ktail = K - 64 * (KB - 1);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int row = 16 * (wave + 8 * j) + (lane >> 2);
-        const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+        const int row = 16 * (wave + 8 * j) + (lane & 15);
+        const int chunk = lane >> 4;
         aoff[j] = wave + 8 * j < R && row0 + row < M ? (uint32_t)(row0 + row) * (uint32_t)K + 16u * chunk : kOOB;
         atail[j] = 16 * chunk < ktail ? aoff[j] : kOOB;
     }
@@ -2275,9 +2280,8 @@ __global__ __launch_bounds__(kW8Threads) void gemm_w8_kernel(const int8_t *__res
         load_to_lds16_so(wbase + (uint32_t)(kGemmBF * 1024) * slot + 1024u * wave, woff, 1024u * (uint32_t)kbc, rw);
     };
 
-    // A operand of row tile i: row 16 i + l % 16, chunk l / 16 (swizzled)
-    const int ard = (lane & 15) * 64 + 16 * ((lane >> 4) ^ ((lane >> 2) & 3));
-    auto read_a = [&](int slot, int i) { return *reinterpret_cast<const v4i *>(&abuf[slot][1024 * i + ard]); };
+    // A operand of row tile i: row 16 i + l % 16, chunk l / 16, at 16 l
+    auto read_a = [&](int slot, int i) { return *reinterpret_cast<const v4i *>(&abuf[slot][1024 * i + 16 * lane]); };
     auto read_w = [&](int slot) { return *reinterpret_cast<const uint4 *>(&wbuf[slot][1024 * wave + 16 * lane]); };
     // decode of raw dword c (k = 16 g + 4 c .. + 3): four table lookups, then
     // the 4 x 3 byte transpose into dword c of the three B operands
@@ -3111,22 +3115,28 @@ GemmPlan gemm_plan_rt(int64_t M, int64_t K, int64_t N, int rt, int splits) {
     return p;
 }
 
-// Tile height: 2, 4 or 5 row tiles of 32 per wave, the one with the least
+// Tile height: 64, 128 or 160 token rows (rt = 2, 4, 5: the four-wave
+// kernel's 32-row tiles per wave; 128 and 160 rows run on the eight-wave
+// kernel).  When the 64-row tiles all fit one round on the CUs, they are
+// taken: the kernel then lasts one workgroup's time, which is least for the
+// smallest tile (the vision down-projection, 104 tiles of 64 rows: 46.7 us
+// against 51.2 us on 52 tiles of 128).  Otherwise the one with the least
 // estimated time at one workgroup per CU: workgroup rounds x (64-column
 // blocks x clocks per block + a fixed prologue and epilogue), with the
-// clocks measured on this part.  Taller tiles reuse each decoded weight
-// over more rows; shorter ones make more workgroups, which pays when the
-// taller tiles leave CUs idle (the vision down-projection: 52 tiles of 128
-// rows, 104 of 64).
+// clocks measured on this part (the eight-wave figures from timestamps
+// inside the kernel: 1283 and 1612 clk per block, 12500 and 14000 fixed).
+// Taller tiles reuse each decoded weight over more rows; shorter ones make
+// more workgroups, which pays when the taller tiles leave CUs idle.
 int gemm_rt(int64_t M, int64_t K, int64_t N, int cus) {
     const int64_t T = (N + 2) / 3;
     const int64_t nbn = ((T + 15) / 16 + kGemmBF - 1) / kGemmBF;
     const int64_t KB = (K + 63) / 64;
+    if ((M + 63) / 64 * nbn <= cus) return 2;
     auto cost = [&](int rt, int64_t clk_block, int64_t clk_fixed) {
         const int64_t tiles = (M + 32 * rt - 1) / (32 * rt) * nbn;
         return (tiles + cus - 1) / cus * (KB * clk_block + clk_fixed);
     };
-    const int64_t c2 = cost(2, kClkBlockRT2, 18000), c4 = cost(4, 1400, 26000), c5 = cost(5, 1663, 30000);
+    const int64_t c2 = cost(2, kClkBlockRT2, 18000), c4 = cost(4, 1283, 12500), c5 = cost(5, 1612, 14000);
     return c5 < c4 && c5 < c2 ? 5 : c2 < c4 ? 2 : 4;
 }
 
