@@ -1450,7 +1450,9 @@ __global__ __launch_bounds__(1024) void gemv_codes_kernel(const int8_t *__restri
 // --------------------------------------------------------------- GEMM
 
 // Prefill GEMM for many token rows: INT8 activations x decoded S3D8 weights
-// on v_mfma_i32_32x32x32_i8 (INT32 accumulation).
+// on v_mfma_i32_32x32x32_i8 (INT32 accumulation), one wave per SIMD.  The
+// library runs it for 64-row tiles and for every split-K launch; 128- and
+// 160-row tiles without split-K run on the eight-wave kernel further down.
 //
 // Workgroup tile = 32 RT token rows x 128 channel triples (384 output
 // channels), RT = 2, 4 or 5; 4 waves side by side along N, each 32 RT rows x
@@ -3171,29 +3173,32 @@ int launch_gemm(const GemmPlan &p, const int8_t *xq, const float *xs, int64_t M,
                 const uint8_t *tiled, const uint32_t *table32, bool f3d8, const uint16_t *scales_bf16, void *y,
                 bool obf, int32_t *acc_out, void *ws, hipStream_t stream) {
     if (p.grid > 2147483647) return s3d8::fail(S3D8_ERR_SHAPE, "problem too large");
-#define S3D8_GEMM_RT(rt, sk)                                                         \
-    {{gemm_kernel<rt, false, false, sk>, gemm_kernel<rt, false, true, sk>},          \
-     {gemm_kernel<rt, true, false, sk>, gemm_kernel<rt, true, true, sk>}}
-#define S3D8_GEMM_BUILDS(sk) {S3D8_GEMM_RT(2, sk), S3D8_GEMM_RT(4, sk), S3D8_GEMM_RT(5, sk)}
-    static const GemmFn fns[2][3][2][2] = {S3D8_GEMM_BUILDS(false), S3D8_GEMM_BUILDS(true)};
-#undef S3D8_GEMM_BUILDS
-#undef S3D8_GEMM_RT
     const bool split = p.splits > 1;
+    // 128- and 160-row tiles without split-K: the eight-wave kernel
     if ((p.rt == 4 || p.rt == 5) && !split) {
         typedef void (*W8Fn)(const int8_t *, const uint8_t *, const uint32_t *, int, int, int, int, int, int, int,
                              const float *, const uint16_t *, void *, int32_t *);
-#define S3D8_W8(r) {{gemm_w8_kernel<r, false, false>, gemm_w8_kernel<r, false, true>}, \
-                    {gemm_w8_kernel<r, true, false>, gemm_w8_kernel<r, true, true>}}
+#define S3D8_W8(r)                                                                    \
+    {{gemm_w8_kernel<r, false, false>, gemm_w8_kernel<r, false, true>},              \
+     {gemm_w8_kernel<r, true, false>, gemm_w8_kernel<r, true, true>}}
         static const W8Fn w8[2][2][2] = {S3D8_W8(8), S3D8_W8(10)};
 #undef S3D8_W8
-        hipLaunchKernelGGL(w8[p.rt == 5][acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(kW8Threads), 0, stream, xq, tiled,
-                           table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn, (int)f3d8, xs,
-                           scales_bf16, y, acc_out);
+        hipLaunchKernelGGL(w8[p.rt == 5][acc_out != nullptr][obf], dim3((unsigned)p.grid), dim3(kW8Threads), 0,
+                           stream, xq, tiled, table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn,
+                           (int)f3d8, xs, scales_bf16, y, acc_out);
         return launch_status();
     }
+    // the four-wave kernel: 64-row tiles, and every split-K launch
+#define S3D8_GEMM_RT(rt, sk)                                                         \
+    {{gemm_kernel<rt, false, false, sk>, gemm_kernel<rt, false, true, sk>},          \
+     {gemm_kernel<rt, true, false, sk>, gemm_kernel<rt, true, true, sk>}}
+    static const GemmFn fns[4][2][2] = {S3D8_GEMM_RT(2, false), S3D8_GEMM_RT(2, true), S3D8_GEMM_RT(4, true),
+                                        S3D8_GEMM_RT(5, true)};
+#undef S3D8_GEMM_RT
     int32_t *cnt = split ? static_cast<int32_t *>(ws) : nullptr;
     int32_t *part = split ? reinterpret_cast<int32_t *>(static_cast<char *>(ws) + p.ws_cnt_bytes) : nullptr;
-    hipLaunchKernelGGL(fns[split][p.rt == 2 ? 0 : p.rt == 4 ? 1 : 2][acc_out != nullptr][obf], dim3((unsigned)p.grid),
+    const int variant = split ? (p.rt == 2 ? 1 : p.rt == 4 ? 2 : 3) : 0;
+    hipLaunchKernelGGL(fns[variant][acc_out != nullptr][obf], dim3((unsigned)p.grid),
                        dim3(256), 0, stream,
                        xq, tiled, table32, (int)M, (int)K, (int)N, (int)((N + 2) / 3), p.nbm, p.nbn, (int)f3d8,
                        p.splits, p.kbper, xs, scales_bf16, y, acc_out, cnt, part, (uint32_t)p.ws_part_bytes);
