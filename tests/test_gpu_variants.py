@@ -217,3 +217,34 @@ def test_c3_prefill_3d8_bf16_sampled_rows(gpu):
     rows = np.array([0, 1, 127, 128, 159, 160, 1023, 2047])
     ref = oracle_path(x[rows], T3, alpha, packed, lin.N, "3d8")
     compare(tuple(g[rows] for g in got), ref, "bf16")
+
+
+# ------------------------------------------------------------------ 3D8 without accumulators
+# The GEMMs are built separately for the call that stores no INT32
+# accumulators (the one the benchmark times); the format is a run-time flag
+# inside each build, so these cover the 3D8 table path of the accumulator-free
+# builds: 64-row tiles (M = 300), 128-row tiles (M = 600) and 160-row tiles
+# (M = 1270 and 2000, with N mod 3 = 2), whole and split into column ranges.
+Y_ONLY = [("linear", 300, 1040, 772), ("linear", 600, 80, 12280), ("linear", 1270, 80, 12280),
+          ("linear", 2000, 1024, 14335), ("splitk", 600, 1040, 12280)]
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,M,K,N", Y_ONLY)
+def test_3d8_without_accumulators_matches_oracle(gpu, kind, M, K, N, out):
+    table, alpha, packed = fmt_inputs([3020, M, K, N], N, K, "3d8")
+    x = workloads.gaussian_matrix([3021, M, K], M, K)
+    _, _, _, y_r = oracle_path(x, table, alpha, packed, N, "3d8")
+    tiled = s3d8.tile(dev(packed, gpu), N)
+    t = dev(table, gpu)
+    s = dev(alpha.view(np.int16), gpu)
+    xq, xs = s3d8.quant_act(dev(x, gpu))
+    if kind == "splitk":
+        y = s3d8.linear_splitk(xq, xs, tiled, t, s, N, splits=3, fmt="3d8", out=out)
+    else:
+        y = s3d8.linear(xq, xs, tiled, t, s, N, fmt="3d8", out=out)
+    torch.cuda.synchronize()
+    if out == "bf16":
+        np.testing.assert_array_equal(bf16_bits(y), oracle.to_bf16(y_r))
+    else:
+        check_y(y.cpu().numpy(), y_r)
