@@ -124,11 +124,12 @@ def test_prefill_full_output_matches_oracle(gpu, name, path, mode):
 
 # ------------------------------------------------------------------ ragged shapes, every mode
 # (M, K, N): row tails of every row-tile height (1270 and 2000 take
-# 160-row tiles, 600 takes 128-row tiles, 300, 33 and 17 take 64-row tiles),
-# ragged triples (N mod 3 = 1, 2), K past the last 64-column block, and
-# small M through the GEMV kernels.
-RAGGED = [(1270, 80, 12280), (2000, 1024, 14335), (600, 80, 12280), (300, 1040, 772), (33, 1040, 97),
-          (17, 80, 50), (16, 1040, 97), (9, 256, 48), (5, 64, 47), (1, 4096, 300)]
+# 160-row tiles, 600 and 640 take 128-row tiles, 300, 33 and 17 take 64-row
+# tiles), ragged triples (N mod 3 = 1, 2, on every tile height), K past the
+# last 64-column block, and small M through the GEMV kernels.
+RAGGED = [(1270, 80, 12280), (2000, 1024, 14335), (2000, 144, 14339), (600, 80, 12280), (640, 144, 12281),
+          (300, 1040, 772), (33, 1040, 97), (17, 80, 50), (16, 1040, 97), (9, 256, 48), (5, 64, 47),
+          (1, 4096, 300)]
 
 
 @pytest.mark.parametrize("name,splits", [("vision_down", 2), ("vision_down", 3), ("vision_down", 5),

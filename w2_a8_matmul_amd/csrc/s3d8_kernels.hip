@@ -2141,7 +2141,8 @@ constexpr int kW8Threads = 512;
 // past N).  Branch-free as store_tile_rows: rows past M and channels past N
 // get an out-of-range offset and their stores are dropped; a lane whose
 // triple straddles N stores its valid channels one by one in a second pass.
-// kBF: bfloat16 outputs, one 2-byte store per channel.
+// kBF: bfloat16 outputs, a 4-byte and a 2-byte store per row (one 2-byte
+// store per channel when the accumulators are stored as well).
 template <int R, bool kAcc, bool kBF>
 __device__ __forceinline__ void store_rows16(const v4i (&acc)[R][3], const float *xsl, int M, int N,
                                              int row0, int g, const float (&sc)[3], const uint32_t (&coff)[3],
@@ -2155,7 +2156,11 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[R][3], const float
     auto dead = [&](int r) { return (uint32_t)(nrows - 1 - r) & kOOB; };
     auto outf = [&](int i, int v, int d) { return (sx[i][v] * (float)acc[i][d][v]) * sc[d]; };
     auto out = [&](int i, int v, int d) { return __float_as_uint(outf(i, v, d)); };
-    if constexpr (kBF) {
+    typedef uint32_t u3 __attribute__((ext_vector_type(3)));
+    const bool split = coff[0] != kOOB && coff[2] == kOOB;
+    if constexpr (kBF && kAcc) {
+        // with the accumulators as well: one 2-byte store per channel beside
+        // each accumulator (the packed stores below made this build spill)
         const uint32_t yrowb = 2u * (uint32_t)N;
         const auto ry = make_rsrc(static_cast<uint16_t *>(y) + (int64_t)row0 * N, yrowb * (uint32_t)nrows);
 #pragma unroll
@@ -2168,16 +2173,52 @@ __device__ __forceinline__ void store_rows16(const v4i (&acc)[R][3], const float
                     const uint32_t yo = coff[d] == kOOB ? kOOB : coff[d] >> 1;
                     __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(outf(i, v, d)), ry,
                                                           (yo + (uint32_t)r * yrowb) | dead(r), 0, 0);
-                    if constexpr (kAcc)
-                        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][d][v], ra,
-                                                              (coff[d] + (uint32_t)r * rowb) | dead(r), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)acc[i][d][v], ra,
+                                                          (coff[d] + (uint32_t)r * rowb) | dead(r), 0, 0);
+                }
+            }
+        return;
+    } else if constexpr (kBF) {
+        // Triple t's three bf16 channels are bytes 6t .. 6t + 5 of a row: for
+        // even t a 4-byte-aligned pair (channels 0, 1) and a halfword, for
+        // odd t a halfword and an aligned pair (channels 1, 2), so two stores
+        // per row instead of three.  (Lane parity is triple parity: the
+        // wave's first triple is a multiple of 16.)  A triple that straddles
+        // N stores its valid channels one by one in a second pass.
+        const uint32_t yrowb = 2u * (uint32_t)N;
+        const auto ry = make_rsrc(static_cast<uint16_t *>(y) + (int64_t)row0 * N, yrowb * (uint32_t)nrows);
+        const bool odd = (threadIdx.x & 1) != 0;
+        const uint32_t b0 = split ? kOOB : (coff[0] == kOOB ? kOOB : coff[0] >> 1);
+        const uint32_t o32 = odd ? b0 + 2u : b0, o16 = odd ? b0 : b0 + 4u;
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * g + v;
+                const uint32_t h0 = f32_to_bf16_rne(outf(i, v, 0)), h1 = f32_to_bf16_rne(outf(i, v, 1)),
+                               h2 = f32_to_bf16_rne(outf(i, v, 2));
+                const uint32_t pair = odd ? (h1 | (h2 << 16)) : (h0 | (h1 << 16));
+                __builtin_amdgcn_raw_buffer_store_b32(pair, ry, (o32 + (uint32_t)r * yrowb) | dead(r), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(odd ? h0 : h2), ry,
+                                                      (o16 + (uint32_t)r * yrowb) | dead(r), 0, 0);
+            }
+        if (__builtin_amdgcn_ballot_w64(split) == 0) return;
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int r = 16 * i + 4 * g + v;
+                const uint32_t dd = dead(r) | (split ? 0u : kOOB);
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const uint32_t yo = coff[d] == kOOB ? kOOB : coff[d] >> 1;
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(outf(i, v, d)), ry,
+                                                          (yo + (uint32_t)r * yrowb) | dd, 0, 0);
                 }
             }
         return;
     }
-    typedef uint32_t u3 __attribute__((ext_vector_type(3)));
     const auto ry = make_rsrc(static_cast<float *>(y) + (int64_t)row0 * N, rowb * (uint32_t)nrows);
-    const bool split = coff[0] != kOOB && coff[2] == kOOB;
     const uint32_t base3 = split ? kOOB : coff[0];
 #pragma unroll
     for (int i = 0; i < R; ++i)
